@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: the fused
+forward (O and LSE) followed by the recompute backward (D, dK/dV, dQ) at
+B=2, H=12, N=8192, d=64, fp16, non-causal (the A100 table's shape at its
+largest N).  Inputs are resident in HBM before timing starts.
+
+Credited flops (the metric's convention): forward 4*B*H*N^2*d, backward 2.5x
+that (both halved for causal).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 MFMA peak
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_traffic.json")
+FWD_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--N", type=int, default=8192)
+    ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time only the forward (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="heads of the workload the CPU oracle runs for its baseline")
+    return ap.parse_args()
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for rel in FWD_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(per_launch_bytes_algo):
+    """HBM bytes per forward launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on different kernel sources."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256_16") != sources_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, heads):
+    """The fp64 oracle as it stands, on `heads` heads of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q, k, v, do = (w.f64(n) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    for idx in range(heads):
+        b, h = divmod(idx, w.H)
+        oracle.forward_head(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
+        oracle.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * 4.0 * w.N * w.N * w.d * heads * (0.5 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads, forward+backward in float64 "
+                      f"({dt:.1f} s), credited flops as for the GPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the path shards by heads with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import io_aware_exact_08_amd as fa
+    from synth import inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = si.a100_sweep(args.N, with_do=True)
+    if args.causal:
+        w.causal = True
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.float16).to(dev)
+
+    q, k, v, do = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.do)
+    B, H, N, d = w.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        if not args.fwd_only:
+            fa.flash_attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale,
+                              dq=dq, dk=dk, dv=dv, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [] if args.fwd_only else [e[1].elapsed_time(e[2]) for e in events]
+    ms_per_step = wall * 1e3 / args.steps
+    causal_f = 0.5 if w.causal else 1.0
+    fwd_flops = 4.0 * B * H * N * N * d * causal_f
+    bwd_flops = 2.5 * fwd_flops
+    step_flops = fwd_flops + (0.0 if args.fwd_only else bwd_flops)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    fwd_avg = float(np.mean(fwd_ms))
+    fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12
+    res = {
+        "metric": "attention fwd(+bwd) TFLOP/s on 1 MI355X and % of MFMA peak, B=2 H=12 d=64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("forward" if args.fwd_only else "forward+backward")
+                        + f" exact attention B={B} H={H} N={N} d={d} fp16 "
+                        + ("causal" if w.causal else "non-causal"),
+            "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+            "accumulate": "f32", "parallelism": "single GPU",
+        },
+        "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_avg, 4), "tflops": round(fwd_tflops, 2),
+                "frac_of_peak": round(fwd_tflops / PEAK_MFMA_F16_TFLOPS, 4)},
+    }
+    if bwd_ms:
+        bwd_avg = float(np.mean(bwd_ms))
+        res["bwd"] = {"ms": round(bwd_avg, 4),
+                      "tflops_credited": round(bwd_flops / (bwd_avg * 1e-3) / 1e12, 2),
+                      "kernels": "bwd_pre + bwd_dkdv + bwd_dq"}
+    # Roofline of the forward kernel: algorithmic flops per launch over its
+    # average event-timed duration in the timed region.
+    res["roofline"] = {
+        "kernel": "fwd_kernel<64,f16,non-causal>" if not w.causal else "fwd_kernel<64,f16,causal>",
+        "bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_MFMA_F16_TFLOPS, 4),
+        "traffic": traffic_from_profile(None),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

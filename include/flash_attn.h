@@ -1,0 +1,119 @@
+/*
+ * flash_attn.h - C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * Operation (page 1, examples 1-3; page 2, "Kernel Fusion" and "Tiling"):
+ *     O = softmax(scale * Q K^T) V          softmax over the key axis
+ * computed exactly (not approximated) by one fused kernel that streams K/V
+ * tiles through on-chip memory under an online softmax, and the backward of
+ * page 2, "Re-computation", which rebuilds the probabilities blockwise from the
+ * saved row log-sum-exp instead of storing the N x N matrix.
+ *
+ * Conventions shared by every entry point
+ *  - Layout: Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] with d
+ *    innermost (element (b,h,i,c) at ((b*H + h)*N + i)*d + c), the layout of
+ *    page 1, example 2.  LSE and the backward workspace are [B, H, N] float32.
+ *  - Pointers are DEVICE pointers (HIP global memory) of the calling process's
+ *    current device.  Every tensor pointer must be 16-byte aligned.
+ *  - Ownership: the caller allocates and frees every buffer.  The library never
+ *    allocates device memory and keeps no mutable global state; calls are
+ *    thread-safe.  Inputs are read-only; outputs are fully overwritten.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns before it runs.  Faults inside the kernels
+ *    surface at the caller's next synchronisation.
+ *  - Errors: the return value is a fa_status.  Arguments are validated before
+ *    anything is enqueued; on a non-zero status nothing was launched.
+ *  - Sizes: B, H, N >= 1, any N (tail tiles are masked); d in {64, 128};
+ *    B*H*N*d < 2^31 elements per tensor.
+ *  - Causal: key j is visible to query i iff j <= i (queries and keys share the
+ *    same length N).
+ *  - Arithmetic: fp16 or bf16 operands, float32 accumulation and softmax state,
+ *    probabilities rounded to the operand type (round-to-nearest-even) before
+ *    the P V product.
+ */
+#ifndef FLASH_ATTN_H_
+#define FLASH_ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL                       */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 elements  */
+  FA_ERR_HEADDIM = 3,   /* d not in {64, 128}                               */
+  FA_ERR_DTYPE = 4,     /* unknown fa_dtype                                 */
+  FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                 */
+  FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */
+  FA_ERR_WORKSPACE = 7, /* backward workspace missing or too small          */
+  FA_ERR_SCALE = 8      /* scale is not a finite positive number            */
+} fa_status;
+
+/* Element types: Q/K/V (and dQ/dK/dV) type x O (and dO) type. */
+typedef enum {
+  FA_F16 = 0,          /* fp16 in, fp16 O                                   */
+  FA_BF16 = 1,         /* bf16 in, bf16 O                                   */
+  FA_F16_OUT_F32 = 2,  /* fp16 in, float32 O                                */
+  FA_BF16_OUT_F32 = 3  /* bf16 in, float32 O                                */
+} fa_dtype;
+
+/*
+ * Forward.  Page 2, "Kernel Fusion" (one kernel; only the output reaches
+ * global memory) and "Tiling" (B_q x B_k tiles, online softmax: per-tile max
+ * and exp-sum, running max update with rescaled normaliser, one final
+ * normalisation).
+ *
+ *   q, k, v : [B,H,N,d] of the input type (read)
+ *   o       : [B,H,N,d] of the output type (written)
+ *   lse     : [B,H,N] float32 (written), LSE_i = ln sum_{j visible}
+ *             exp(scale * q_i . k_j), natural log with the scale included; the
+ *             backward rebuilds P_ij = exp(scale * q_i . k_j - LSE_i) from it.
+ *   scale   : finite, > 0 (usually 1/sqrt(d))
+ *   causal  : 0 or 1
+ *   dtype   : fa_dtype
+ *   stream  : hipStream_t
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void* stream);
+
+/*
+ * Backward.  Page 2, "Re-computation": scores are not cached; P is recomputed
+ * per tile from Q, K and the forward's LSE.  Gradients of L = <dO, O>:
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+ *   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Three kernels on `stream`: D (one pass over O and dO), dK/dV (each workgroup
+ * keeps a K/V tile and loops over query tiles, the loop order of that
+ * section), dQ (each workgroup keeps a query tile and loops over K/V tiles).
+ * No atomics: results are deterministic.
+ *
+ *   q, k, v, o, lse : as produced for / by flash_attn_fwd (read)
+ *   dout            : [B,H,N,d] gradient of O, of O's type (read)
+ *   dq, dk, dv      : [B,H,N,d] of the input type (written)
+ *   workspace       : device buffer of >= flash_attn_bwd_workspace_bytes(...)
+ *                     bytes, 16-byte aligned, owned by the caller; its
+ *                     contents on entry do not matter and on return are
+ *                     unspecified.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, int causal, int dtype,
+                   void* stream);
+
+/* Bytes of workspace flash_attn_bwd needs (4 * B * H * N: one float per row). */
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Static, NUL-terminated description of a status code. */
+const char* flash_attn_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int flash_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H_ */

@@ -1,0 +1,120 @@
+"""Exact scaled-dot-product attention for MI355X (gfx950).
+
+The computation runs entirely in the HIP library ``libflash_attn.so``; this
+module only marshals torch tensors (device memory and streams) into its C ABI:
+
+    flash_attn_fwd(q, k, v, causal=False, scale=None, out_f32=False) -> (o, lse)
+    flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+
+Layout [B, H, N, d], d in {64, 128}, fp16 or bf16 inputs.
+"""
+from __future__ import annotations
+
+import math
+
+from . import _lib
+from ._lib import FlashAttnError, status_string  # noqa: F401
+
+__all__ = ["flash_attn_fwd", "flash_attn_bwd", "FlashAttnError", "status_string",
+           "dtype_code", "workspace_bytes"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(in_dtype, out_f32: bool) -> int:
+    torch = _torch()
+    if in_dtype == torch.float16:
+        return _lib.FA_F16_OUT_F32 if out_f32 else _lib.FA_F16
+    if in_dtype == torch.bfloat16:
+        return _lib.FA_BF16_OUT_F32 if out_f32 else _lib.FA_BF16
+    raise TypeError(f"unsupported input dtype {in_dtype}; expected float16 or bfloat16")
+
+
+def _check(t, name, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes_stream(torch.cuda.current_stream(t.device))
+
+
+def ctypes_stream(s):
+    return s.cuda_stream
+
+
+def workspace_bytes(B, H, N, d) -> int:
+    return _lib.flash_attn_bwd_workspace_bytes(B, H, N, d)
+
+
+def flash_attn_fwd(q, k, v, causal: bool = False, scale=None, out_f32: bool = False,
+                   o=None, lse=None):
+    """Forward: returns (o [B,H,N,d], lse [B,H,N] float32).
+
+    ``o``/``lse`` may be passed to write into existing buffers.  ``scale``
+    defaults to 1/sqrt(d), rounded to float32.
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    code = dtype_code(q.dtype, out_f32)
+    odt = torch.float32 if out_f32 else q.dtype
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    _check(o, "o", (B, H, N, d), odt)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, H, N, d, sc, int(bool(causal)), code, _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd")
+    return o, lse
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None,
+                   dq=None, dk=None, dv=None, workspace=None):
+    """Backward: returns (dq, dk, dv) in the input dtype.
+
+    ``o`` is the forward output (input dtype or float32); ``dout`` has the
+    input dtype.  The workspace (4*B*H*N bytes) is allocated here unless given.
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    out_f32 = o.dtype == torch.float32
+    _check(o, "o", (B, H, N, d), o.dtype)
+    if not out_f32 and o.dtype != q.dtype:
+        raise TypeError("o must have the input dtype or float32")
+    _check(lse, "lse", (B, H, N), torch.float32)
+    code = dtype_code(q.dtype, out_f32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    nbytes = workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=q.device)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(),
+                             B, H, N, d, sc, int(bool(causal)), code, _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd")
+    return dq, dk, dv

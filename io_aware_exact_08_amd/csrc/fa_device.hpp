@@ -1,0 +1,127 @@
+// Device-side building blocks for the gfx950 attention kernels: operand
+// vector types, the 32x32x16 MFMA, RNE pair conversion, LDS swizzles and the
+// register-layout permutations that let the score accumulator feed the P.V
+// product without an LDS round trip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// C[32x32] += A[32x16] * B[16x32], fp32 accumulate.  Lane l supplies row (l%32)
+// of A and column (l%32) of B, eight k-values each; lanes l and l+32 supply
+// complementary k-halves.  A k-slot of A pairs with the same k-slot of B, so
+// any consistent assignment of physical indices to slots gives the same sum.
+// Output: lane l holds column l%32, register r holds row 8*(r/4)+4*(l/32)+r%4.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two floats -> two 16-bit values in one dword, round-to-nearest-even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (BF16) {
+    bf16x2 v;
+    v.x = (__bf16)lo;
+    v.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    f16x2 v;
+    v.x = (_Float16)lo;
+    v.y = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  if constexpr (BF16) {
+    return __uint_as_float(((uint32_t)bits) << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+}
+
+// acc + lo + hi of a packed pair of 16-bit values (v_dot2c_f32_{f16,bf16}
+// against (1, 1)): the products are exact, the sum is in fp32.
+template <bool BF16>
+__device__ __forceinline__ float sum2(uint32_t w, float acc) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3C003C00u),
+                                  acc, false);
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine a value with the one held by lane l^32 (the other half of the
+// wave) using v_permlane32_swap: with both operands x, lane l < 32 receives
+// (x_l, x_{l+32}) and lane l >= 32 receives (x_{l-32}, x_l).  The max and the
+// (commutative) sum are then identical in both halves.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Row permutation applied when loading the A operand of a 32x32 MFMA so that
+// the output's register r of lane half h maps to row 16*(r/8) + 8*h + r%8:
+// each lane then holds, per 16-row chunk, eight consecutive rows - exactly the
+// k-slots of the next MFMA's operand.  (Swaps bits 2 and 3 of the row.)
+__device__ __forceinline__ int perm_k(int m) {
+  return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// Row permutation so that output register r of lane half h maps to row
+// 16*h + r: each lane holds sixteen consecutive rows (contiguous stores).
+__device__ __forceinline__ int perm_o(int m) {
+  return (((m >> 2) & 1) << 4) | ((m >> 3) << 2) | (m & 3);
+}
+
+// 16-byte-chunk XOR swizzles (in units of 8 16-bit elements) for LDS tiles.
+// Row-major [rows][cols] tile read as MFMA A operand with rows perm_k(m):
+// distinct over each group of 8 lanes.
+__device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+// Transposed [d][keys] tile: distinct over the rows perm_o(m) of 8 lanes and
+// over rows 8*c + i (c = 0..7) written by 8 lanes.
+__device__ __forceinline__ int swz_t(int d) {
+  return ((d ^ (d >> 3)) & 1) | ((((d >> 1) ^ (d >> 5)) & 1) << 1) | (((d >> 4) & 1) << 2);
+}
+
+// Byte-select of two dwords: result bytes picked by `sel` (v_perm_b32).
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  // (a.lo16, b.lo16)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  // (a.hi16, b.hi16)
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+}  // namespace fa

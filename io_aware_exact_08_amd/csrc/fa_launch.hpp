@@ -1,0 +1,48 @@
+// Host-side launchers shared by the C-ABI entry points and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// dtype codes (same values as fa_dtype in include/flash_attn.h)
+constexpr int kF16 = 0, kBF16 = 1, kF16OutF32 = 2, kBF16OutF32 = 3;
+
+struct FwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int BH;
+  int N;
+  int d;
+  float scale;
+  bool causal;
+  int dtype;
+};
+
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [BH*N] workspace
+  int BH;
+  int N;
+  int d;
+  float scale;
+  bool causal;
+  int dtype;
+};
+
+hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,106 @@
+// C-ABI entry points: argument validation, then one enqueue on the caller's
+// stream.  Declarations, argument meaning and error behaviour are documented
+// in include/flash_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/flash_attn.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  const long long elems = (long long)B * H * N * d;
+  if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (dtype < FA_F16 || dtype > FA_BF16_OUT_F32) return FA_ERR_DTYPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  fa::FwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = B * H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  return fa::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                   int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  fa::BwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = (float*)workspace;
+  p.BH = B * H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, causal 0/1)";
+    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "unknown dtype code";
+    case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_WORKSPACE: return "backward workspace missing or too small";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    default: return "unknown status";
+  }
+}
+
+int flash_attn_version(void) { return 100; }
+
+}  // extern "C"
