@@ -36,8 +36,11 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1,
+    ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the CPU oracle runs for its baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB before the "
+                         "timed loop (reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -127,6 +130,14 @@ def main():
                               dq=dq, dk=dk, dv=dv, workspace=ws)
             if ev is not None:
                 ev[2].record(stream)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

@@ -21,6 +21,10 @@ HIPCC_FLAGS = [
     # keep the compiler away from packed fp32 VALU forms
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # MFMA accumulators in VGPRs (no AGPR copies around the softmax)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # no NaN canonicalisation in max (infinities are still honoured)
+    "-fno-honor-nans",
 ]
 
 

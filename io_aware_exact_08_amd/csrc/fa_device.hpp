@@ -37,6 +37,52 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// Raw buffer access.  A resource covers [base, base + bytes); loads outside it
+// return 0 and stores outside it are dropped by the hardware, which handles
+// ragged tails without branches.
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data format
+
+__device__ __forceinline__ brsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 bload16(brsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void bstore16(u32x4 v, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
+                                         r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore4(float v, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+}
+
+// Direct buffer -> LDS load of 16 bytes per lane: lane l of the wave writes
+// lds_base + 16*l (lds_base must be wave-uniform); out-of-range reads land as
+// zeros.  Completion is tracked by vmcnt, see wait_vmem().
+__device__ __forceinline__ void bload16_lds(brsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most K vector-memory operations of this wave are outstanding.
+template <int K>
+__device__ __forceinline__ void wait_vmem_keep() {
+  static_assert(K >= 0 && K < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte rows loaded by lanes
+// 4*j + i/4, j = 0..3 (element j of the result).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_byte_addr) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)lds_byte_addr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Two floats -> two 16-bit values in one dword, round-to-nearest-even.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -108,6 +154,9 @@ __device__ __forceinline__ int perm_o(int m) {
 // Row-major [rows][cols] tile read as MFMA A operand with rows perm_k(m):
 // distinct over each group of 8 lanes.
 __device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+// Row-major V tile read through lds_read_tr16: rows 4 apart share a bank
+// window, so chunks are XORed with s(row % 4) in {0, 1, 4, 5}.
+__device__ __forceinline__ int swz_v(int r) { return (r & 1) | ((r & 2) << 1); }
 // Transposed [d][keys] tile: distinct over the rows perm_o(m) of 8 lanes and
 // over rows 8*c + i (c = 0..7) written by 8 lanes.
 __device__ __forceinline__ int swz_t(int d) {

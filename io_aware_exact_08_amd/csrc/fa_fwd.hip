@@ -15,10 +15,17 @@
 //  * K rows are fed to the MFMA with bits 2 and 3 of the row swapped, which
 //    makes each lane hold 8 consecutive keys per 16-key chunk: the rounded
 //    probabilities are then directly the B operand of O^T += V^T P^T.
-//  * K tiles sit row-major in LDS; V tiles are transposed to [d][key] while
-//    being written to LDS so the V^T operand is one 16-byte read per lane.
-//    Both are double-buffered: tile j+1 is fetched from HBM into registers
-//    while tile j is multiplied, then written to the other LDS buffer.
+//  * K and V tiles sit row-major in LDS, double-buffered, and are filled by
+//    direct buffer->LDS loads (no staging registers): tile j+1 is in flight
+//    while tile j is multiplied.  The V^T operand of O^T += V^T P^T is read
+//    with the transposing ds_read_b64_tr_b16 (two per MFMA).  Both tiles use
+//    16-byte-chunk XOR swizzles chosen so every operand read is free of bank
+//    conflicts; the swizzle is applied by choosing each lane's source address,
+//    since a direct load writes lanes to consecutive LDS slots.
+//  * Global traffic uses raw buffer instructions: reads past the end of a
+//    head return 0 and stores past it are dropped, so ragged tails need no
+//    branches; only tiles that straddle the end or the causal diagonal run
+//    the masked copy of the tile body.
 //  * fp16 rescaling is lazy: the running max used in the exponent is only
 //    raised when a row's new max exceeds it by more than 8 (log2 units).  Any
 //    common reference value gives the same O = acc / l and LSE = m + log2 l
@@ -35,26 +42,43 @@
 //    run on one XCD (consecutive ids are dealt round-robin over the 8 XCDs),
 //    keeping that head's K/V in one L2.  Causal launches issue the heaviest
 //    (last) query tiles first.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 
+#ifndef FA_FWD64_QB
+#define FA_FWD64_QB 1
+#endif
+#ifndef FA_FWD64_BK
+#define FA_FWD64_BK 64
+#endif
+#ifndef FA_FWD_STAGES
+#define FA_FWD_STAGES 4
+#endif
+#ifndef FA_FWD_MIN_WAVES
+#define FA_FWD_MIN_WAVES 2
+#endif
+
 template <int D>
 struct FwdCfg;
 template <>
 struct FwdCfg<64> {
-  static constexpr int QB = 2;   // 32-row query blocks per wave
-  static constexpr int BK = 64;  // keys per tile
+  static constexpr int QB = FA_FWD64_QB;  // 32-row query blocks per wave
+  static constexpr int BK = FA_FWD64_BK;  // keys per tile
 };
 template <>
 struct FwdCfg<128> {
   static constexpr int QB = 1;
-  static constexpr int BK = 64;
+  static constexpr int BK = 32;
 };
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kStages = FA_FWD_STAGES;  // K/V tiles resident in LDS (>= 2)
+
 // Lazy-rescale threshold (log2 units).  bf16 keeps the exact running max
 // (threshold 0): the dominant probability is then exactly 1 and is not
 // rounded, which matters with 8-bit mantissas when one key dominates a row.
@@ -74,22 +98,21 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int QB = FwdCfg<D>::QB;
   constexpr int BK = FwdCfg<D>::BK;
   constexpr int BQ = kWaves * QB * 32;
-  constexpr int DC = D / 16;  // 16-wide d chunks (contraction of S^T)
-  constexpr int DT = D / 32;  // 32-row d tiles of O^T
-  constexpr int KT = BK / 32; // 32-row key tiles of S^T
-  constexpr int KC = BK / 16; // 16-key chunks (contraction of O^T)
-  constexpr int CPR = D / 8;  // 16-byte chunks per K row
-  constexpr int K_LOADS = BK * CPR / kThreads;        // 16B K chunks per thread
-  constexpr int V_LOADS = (BK / 2) * CPR / kThreads;  // row pairs per thread
-  static_assert(K_LOADS * kThreads == BK * CPR, "K tile split");
-  static_assert(V_LOADS * kThreads == (BK / 2) * CPR, "V tile split");
+  constexpr int DC = D / 16;   // 16-wide d chunks (contraction of S^T)
+  constexpr int DT = D / 32;   // 32-row d tiles of O^T
+  constexpr int KT = BK / 32;  // 32-row key tiles of S^T
+  constexpr int KC = BK / 16;  // 16-key chunks (contraction of O^T)
+  constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
+  constexpr int ROWB = D * 2;  // bytes per K/V row
+  constexpr int LOADS = BK * CPR / kThreads;  // 16-byte slots per thread per tile
+  static_assert(LOADS * kThreads == BK * CPR, "tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kStages][BK * D];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -112,72 +135,64 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   }
   const int N = a.N;
   const size_t base = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qg = a.q + base;
-  const uint16_t* __restrict__ Kg = a.k + base;
-  const uint16_t* __restrict__ Vg = a.v + base;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
+  const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
+  const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
   const int qw0 = qt * BQ + wave * (QB * 32);  // first query row of this wave
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query m, half h), slot i
-  // holds d = 16*dc + 8*h + i.
+  // holds d = 16*dc + 8*h + i.  Rows past N read as 0.
   u32x4 qf[QB][DC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + m;
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      if (row < N) {
-        qf[qb][dc] = *(const u32x4*)(Qg + (size_t)row * D + dc * 16 + 8 * h);
-      } else {
-        qf[qb][dc] = u32x4{0, 0, 0, 0};
-      }
+    for (int dc = 0; dc < DC; ++dc)
+      qf[qb][dc] = bload16(rq, (uint32_t)(((qw0 + qb * 32 + m) * D + dc * 16 + 8 * h) * 2), 0);
+
+  // K operand (A of S^T): row kt*32 + perm_k(m), chunk 2dc+h, swizzled.
+  int k_rd[DC];
+  {
+    const int row = perm_k(m);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) k_rd[dc] = (row * D + (((2 * dc + h) ^ swz_row(row)) * 8)) * 2;
+  }
+  // V^T operand (A of O^T) through the transposing read.  In 16-lane group g
+  // (gg = g % 2), lane i = 4j + q reads key 8h + 4r + j (r: which half of the
+  // 8 k-slots) at the 4-element d quad dquad(gg, q) = 16(q%2) + 8gg + 4(q/2)
+  // of d tile dt; lane i then receives d = perm_o(16gg + i) for 4 keys.
+  int v_tr[DT];
+  {
+    const int i = lane & 15, gg = (lane >> 4) & 1;
+    const int j = i >> 2, q = i & 3;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = 4 * dt + 2 * (q & 1) + gg;
+      v_tr[dt] = (8 * h + j) * ROWB + ((chunk ^ swz_v(j)) * 16) + (q >> 1) * 8;
     }
+  }
+  // Direct-load slots: thread slot p = i*256 + tid holds tile row p / CPR at
+  // swizzled chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
+  uint32_t k_gl[LOADS], v_gl[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * kThreads + tid;
+    const int row = p / CPR, cpos = p % CPR;
+    k_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_row(row)) * 16));
+    v_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_v(row)) * 16));
   }
 
   const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
   const int n_kt = (kend + BK - 1) / BK;
 
-  u32x4 kreg[K_LOADS];
-  u32x4 vreg[V_LOADS][2];
-
-  auto load_tile = [&](int j) {
-    const int k0 = j * BK;
+  auto issue_tile = [&](int j, uint16_t* dk, uint16_t* dv) {
+    const uint32_t soff = (uint32_t)(j * BK * ROWB);
 #pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int g = tid + i * kThreads;
-      const int row = g / CPR, c = g % CPR;
-      const int key = k0 + row;
-      kreg[i] = key < N ? *(const u32x4*)(Kg + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int p = tid + i * kThreads;
-      const int c = p % CPR, kp = p / CPR;
-      const int key = k0 + 2 * kp;
-      vreg[i][0] = key < N ? *(const u32x4*)(Vg + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
-      vreg[i][1] = key + 1 < N ? *(const u32x4*)(Vg + (size_t)(key + 1) * D + c * 8)
-                               : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < K_LOADS; ++i) {
-      const int g = tid + i * kThreads;
-      const int row = g / CPR, c = g % CPR;
-      *(u32x4*)(&sK[st][row * D + ((c ^ swz_row(row)) * 8)]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_LOADS; ++i) {
-      const int p = tid + i * kThreads;
-      const int c = p % CPR, kp = p / CPR;
-      const int kk = 2 * kp;  // key offset inside the tile (even)
-      const u32x4 r0 = vreg[i][0], r1 = vreg[i][1];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = c * 8 + e;
-        const uint32_t w = (e & 1) ? hi_halves(r0[e >> 1], r1[e >> 1])
-                                   : lo_halves(r0[e >> 1], r1[e >> 1]);
-        *(uint32_t*)(&sV[st][dd * BK + (((kk >> 3) ^ swz_t(dd)) * 8) + (kk & 7)]) = w;
-      }
+    for (int i = 0; i < LOADS; ++i) {
+      char* kb = (char*)dk + (i * kThreads + wave * 64) * 16;
+      char* vb = (char*)dv + (i * kThreads + wave * 64) * 16;
+      bload16_lds(rk, kb, k_gl[i], soff);
+      bload16_lds(rv, vb, v_gl[i], soff);
     }
   };
 
@@ -194,64 +209,81 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] = f32x16{};
   }
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
   const float c = a.c;
-  for (int j = 0; j < n_kt; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
-    const int k0 = j * BK;
-    const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
-    if (active) {
-      // ---- S^T = K Q^T -------------------------------------------------
-      f32x16 s[QB][KT];
+
+  // S^T = K Q^T for one K tile (the scores of 32*KT keys against this wave's
+  // query blocks).
+  struct Scores {
+    f32x16 v[QB][KT];
+  };
+  auto compute_scores = [&](const uint16_t* Ks) {
+    const char* Kb = (const char*)Ks;
+    Scores sc;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) s[qb][kt] = f32x16{};
+      for (int kt = 0; kt < KT; ++kt) sc.v[qb][kt] = f32x16{};
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const int row = kt * 32 + perm_k(m);
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 af = *(const u32x4*)(&sK[st][row * D + (((2 * dc + h) ^ swz_row(row)) * 8)]);
+      for (int dc = 0; dc < DC; ++dc) {
+        const u32x4 af = *(const u32x4*)(Kb + kt * 32 * ROWB + k_rd[dc]);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kt] = mfma32<BF16>(af, qf[qb][dc], s[qb][kt]);
-        }
+        for (int qb = 0; qb < QB; ++qb) sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
       }
-      // ---- masks (tail keys; causal diagonal) ---------------------------
-      const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = qw0 + qb * 32 + m;
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-              if (key >= N || (CAUSAL && key > qrow)) s[qb][kt][r] = -INFINITY;
-            }
-        }
-      }
-      // ---- online softmax ------------------------------------------------
-      u32x4 pf[QB][KC];
+    return sc;
+  };
+
+  // Online softmax of one tile's scores and O^T += V^T P^T.  MASK: apply the
+  // causal diagonal and the end of the sequence (only on tiles that straddle
+  // them).
+  auto softmax_pv = [&](auto mask_tag, Scores& sc, const uint16_t* Vs, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* Vb = (const char*)Vs;
+    auto& s = sc.v;
+    if constexpr (MASK) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+        const int qrow = qw0 + qb * 32 + m;
+        const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kt][r]);
-        mx = max_halves(mx);
-        const float mnew = mx * c;
-        const bool grow = mnew > m_run[qb] + rescale_threshold<BF16>();
-        if (__ballot(grow) != 0ull) {
-          // Only rows that grew move their reference (the others get alpha = 1
-          // exactly), so every row's result depends on that row's data alone.
-          const float mn = grow ? mnew : m_run[qb];
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+            if (key > lim) s[qb][kt][r] = -INFINITY;
+          }
+      }
+    }
+    // ---- online softmax --------------------------------------------------
+    float mnew[QB];
+    bool grow[QB];
+    bool any_grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          mx0 = fmaxf(mx0, fmaxf(s[qb][kt][r], s[qb][kt][r + 1]));
+          mx1 = fmaxf(mx1, fmaxf(s[qb][kt][r + 2], s[qb][kt][r + 3]));
+        }
+      mnew[qb] = max_halves(fmaxf(mx0, mx1)) * c;
+      grow[qb] = mnew[qb] > m_run[qb] + rescale_threshold<BF16>();
+      any_grow = any_grow || (__ballot(grow[qb]) != 0ull);
+    }
+    // Exponentiate, round, sum and multiply by V^T.  Instantiated twice so
+    // that the path without a rescale carries no merge copies of O.
+    auto finish = [&](auto rescale_tag) {
+      constexpr bool RESCALE = decltype(rescale_tag)::value;
+      u32x4 pf[QB][KC];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (RESCALE) {
+          // Only rows that grew move their reference (the others get
+          // alpha = 1 exactly), so each row depends on its own data alone.
+          const float mn = grow[qb] ? mnew[qb] : m_run[qb];
           const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2(m_run[qb] - mn);
           m_run[qb] = mn;
           l_run[qb] *= alpha;
@@ -260,14 +292,15 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
           for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
         }
         const float neg_m = -m_run[qb];
-        float lsum = 0.f, lsum32 = 0.f;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        float ls32[2] = {0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           float p[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             p[r] = fast_exp2(__builtin_fmaf(s[qb][kt][r], c, neg_m));
-            if constexpr (BF16) lsum32 += p[r];
+            if constexpr (BF16) ls32[r & 1] += p[r];
           }
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
@@ -275,67 +308,115 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               w[e] = pack2<BF16>(p[8 * half + 2 * e], p[8 * half + 2 * e + 1]);
-              lsum = sum2<BF16>(w[e], lsum);
+              ls[e] = sum2<BF16>(w[e], ls[e]);
             }
             pf[qb][2 * kt + half] = w;
           }
         }
-        l_run[qb] += lsum;
-        if constexpr (BF16) l32_run[qb] += lsum32;
+        l_run[qb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if constexpr (BF16) l32_run[qb] += ls32[0] + ls32[1];
       }
-      // ---- O^T += V^T P^T --------------------------------------------------
+      // ---- O^T += V^T P^T -------------------------------------------------
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int drow = dt * 32 + perm_o(m);
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x4 vf = *(const u32x4*)(&sV[st][drow * BK + (((2 * kc + h) ^ swz_t(drow)) * 8)]);
+          const u32x2 lo = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB);
+          const u32x2 hi = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB + 4 * ROWB);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
         }
+    };
+    if (any_grow) {
+      finish(std::true_type{});
+    } else {
+      finish(std::false_type{});
+    }
+  };
+
+  // Software pipeline over K/V tiles, kStages LDS stages deep.  Iteration j
+  // (tile j in stage j % kStages) starts the loads of tile j + kStages - 1,
+  // issues the score MFMAs of tile j + 1 - independent of this tile's softmax,
+  // so the matrix cores have work while the softmax runs on the VALU - then
+  // runs the softmax and P V of tile j.  Before the group barrier it waits
+  // until tile j + 2 has landed (needed by the next iteration's scores).
+  // Direct loads complete in issue order, so this is "all but the newest k".
+  constexpr int kTileLoads = 2 * LOADS;  // direct loads per thread per tile
+  static_assert(kStages == 4, "the pipeline below assumes four stages");
+  auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
+    constexpr int st = decltype(stage_tag)::value;
+    if (j + 3 < n_kt) issue_tile(j + 3, sK[(st + 3) % kStages], sV[(st + 3) % kStages]);
+    if (j + 1 < n_kt) nxt = compute_scores(sK[(st + 1) % kStages]);
+    const int k0 = j * BK;
+    const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
+    if (active) {
+      const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
+      if (need_mask) {
+        softmax_pv(std::true_type{}, cur, sV[st], k0);
+      } else {
+        softmax_pv(std::false_type{}, cur, sV[st], k0);
       }
     }
-    if (j + 1 < n_kt) store_tile(st ^ 1);
+    if (j + 3 < n_kt) {
+      wait_vmem_keep<kTileLoads>();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < 3; ++s0)
+    if (s0 < n_kt) issue_tile(s0, sK[s0], sV[s0]);
+  if (2 < n_kt) {
+    wait_vmem_keep<kTileLoads>();  // tiles 0 and 1 have landed
+  } else {
+    wait_vmem();
+  }
+  __syncthreads();
+  Scores sa = compute_scores(sK[0]);
+  Scores sb;
+  for (int j = 0; j < n_kt; j += 4) {
+    iteration(j, std::integral_constant<int, 0>{}, sa, sb);
+    if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+    if (j + 2 < n_kt) iteration(j + 2, std::integral_constant<int, 2>{}, sa, sb);
+    if (j + 3 < n_kt) iteration(j + 3, std::integral_constant<int, 3>{}, sb, sa);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+  const brsrc_t ro = make_rsrc((const char*)a.o + base * (OUT_F32 ? 4 : 2),
+                               (uint32_t)N * D * (OUT_F32 ? 4 : 2));
+  const brsrc_t rl = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + m;
-    // cross-half sums outside any divergent branch (all 64 lanes take part)
+    const int row = qw0 + qb * 32 + m;  // rows past N are dropped by the stores
     const float lt = sum_halves(l_run[qb]);
     const float ll = BF16 ? sum_halves(l32_run[qb]) : lt;
-    if (row < N) {
-      const float inv = 1.0f / lt;
+    const float inv = 1.0f / lt;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const size_t off = base + (size_t)row * D + dt * 32 + 16 * h;
-        if constexpr (OUT_F32) {
-          float* op = (float*)a.o + off;
+    for (int dt = 0; dt < DT; ++dt) {
+      const int col = dt * 32 + 16 * h;
+      if constexpr (OUT_F32) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f32x4 w;
+        for (int e = 0; e < 4; ++e) {
+          u32x4 w;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) w[t] = oacc[qb][dt][4 * e + t] * inv;
-            *(f32x4*)(op + 4 * e) = w;
-          }
-        } else {
-          uint16_t* op = (uint16_t*)a.o + off;
+          for (int t = 0; t < 4; ++t) w[t] = __float_as_uint(oacc[qb][dt][4 * e + t] * inv);
+          bstore16(w, ro, (uint32_t)((row * D + col + 4 * e) * 4), 0);
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            u32x4 w;
+        for (int e = 0; e < 2; ++e) {
+          u32x4 w;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              w[t] = pack2<BF16>(oacc[qb][dt][8 * e + 2 * t] * inv, oacc[qb][dt][8 * e + 2 * t + 1] * inv);
-            *(u32x4*)(op + 8 * e) = w;
-          }
+          for (int t = 0; t < 4; ++t)
+            w[t] = pack2<BF16>(oacc[qb][dt][8 * e + 2 * t] * inv, oacc[qb][dt][8 * e + 2 * t + 1] * inv);
+          bstore16(w, ro, (uint32_t)((row * D + col + 8 * e) * 2), 0);
         }
       }
-      if (h == 0) {
-        a.lse[(size_t)bh * N + row] = (m_run[qb] + fast_log2(ll)) * kLn2;
-      }
     }
+    if (h == 0) bstore4((m_run[qb] + fast_log2(ll)) * kLn2, rl, (uint32_t)(row * 4), 0);
   }
 }
 
