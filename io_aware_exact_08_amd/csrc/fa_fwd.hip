@@ -26,11 +26,14 @@
 //    head return 0 and stores past it are dropped, so ragged tails need no
 //    branches; only tiles that straddle the end or the causal diagonal run
 //    the masked copy of the tile body.
-//  * fp16 rescaling is lazy: the running max used in the exponent is only
-//    raised when a row's new max exceeds it by more than 8 (log2 units).  Any
-//    common reference value gives the same O = acc / l and LSE = m + log2 l
-//    exactly; the bound keeps every probability below 2^8 so nothing
-//    overflows.  bf16 rescales whenever the max grows (see threshold below).
+//  * fp16 rescaling is lazy and needs no per-tile max: probabilities are
+//    computed against the current reference and, if a row's rounded tile sum
+//    exceeds 2^12 (or the tile is the first), that row alone takes an exact
+//    path that raises its reference to the row max, rescales, and
+//    exponentiates again.  Any common reference value gives the same
+//    O = acc / l and LSE = m + log2 l exactly; the bound keeps every
+//    probability far from fp16 overflow.  bf16 keeps the exact max on every
+//    tile (see the threshold below).
 //  * O is normalised by the sum of the probabilities as rounded for the P V
 //    product (one v_dot2 per pair), so numerator and denominator carry the
 //    same rounding and a dominant key's rounding error cancels.  The fp16
@@ -58,6 +61,9 @@ namespace fa {
 #ifndef FA_FWD_STAGES
 #define FA_FWD_STAGES 4
 #endif
+#ifndef FA_FWD_SCHED_VALU
+#define FA_FWD_SCHED_VALU 12
+#endif
 #ifndef FA_FWD_MIN_WAVES
 #define FA_FWD_MIN_WAVES 2
 #endif
@@ -84,6 +90,9 @@ constexpr int kStages = FA_FWD_STAGES;  // K/V tiles resident in LDS (>= 2)
 // rounded, which matters with 8-bit mantissas when one key dominates a row.
 template <bool BF16>
 constexpr float rescale_threshold() { return BF16 ? 0.0f : 8.0f; }
+// fp16 fast path: largest row sum of rounded probabilities per tile that
+// keeps the current reference.
+constexpr float kLazyBound = 4096.0f;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -109,6 +118,12 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;  // bytes per K/V row
   constexpr int LOADS = BK * CPR / kThreads;  // 16-byte slots per thread per tile
+  // fp16 at d=64 folds the softmax scale into a split Q (see below); bf16 and
+  // d=128 multiply the scores by the scale on the VALU.
+#ifndef FA_FWD_SPLIT
+#define FA_FWD_SPLIT 0
+#endif
+  constexpr bool SPLIT = FA_FWD_SPLIT && !BF16 && D == 64;
   static_assert(LOADS * kThreads == BK * CPR, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][BK * D];
@@ -149,6 +164,28 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[qb][dc] = bload16(rq, (uint32_t)(((qw0 + qb * 32 + m) * D + dc * 16 + 8 * h) * 2), 0);
+
+  // fp16, d=64: fold c = scale*log2(e) into Q as an unevaluated pair c*Q = hi + lo
+  // of fp16 values (about 22 significant bits), so that K Qhi^T + K Qlo^T is
+  // c*s with fp32 accumulation and no per-score multiply.
+  u32x4 qlo[QB][DC];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = qf[qb][dc][e];
+          const float y0 = to_f32<false>((uint16_t)(w & 0xffffu)) * a.c;
+          const float y1 = to_f32<false>((uint16_t)(w >> 16)) * a.c;
+          const uint32_t hi = pack2<false>(y0, y1);
+          const float r0 = y0 - to_f32<false>((uint16_t)(hi & 0xffffu));
+          const float r1 = y1 - to_f32<false>((uint16_t)(hi >> 16));
+          qf[qb][dc][e] = hi;
+          qlo[qb][dc][e] = pack2<false>(r0, r1);
+        }
+  }
 
   // K operand (A of S^T): row kt*32 + perm_k(m), chunk 2dc+h, swizzled.
   int k_rd[DC];
@@ -202,7 +239,9 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   f32x16 oacc[QB][DT];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
+    // Split-path scores carry the reference subtracted inside the MFMA, so it
+    // starts finite; the first tile always re-derives it from the row max.
+    m_run[qb] = SPLIT ? 0.f : -INFINITY;
     l_run[qb] = 0.f;
     l32_run[qb] = 0.f;
 #pragma unroll
@@ -213,23 +252,34 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 
   // S^T = K Q^T for one K tile (the scores of 32*KT keys against this wave's
   // query blocks).
+  // Split path: v = c*s - bias with bias = m_run when the MFMAs were issued
+  // (the accumulators start at -bias); otherwise v = s.
   struct Scores {
     f32x16 v[QB][KT];
+    float bias[QB];
   };
   auto compute_scores = [&](const uint16_t* Ks) {
     const char* Kb = (const char*)Ks;
     Scores sc;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb) {
+      sc.bias[qb] = m_run[qb];
+      f32x16 init;
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) sc.v[qb][kt] = f32x16{};
+      for (int r = 0; r < 16; ++r) init[r] = SPLIT ? -m_run[qb] : 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) sc.v[qb][kt] = init;
+    }
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const u32x4 af = *(const u32x4*)(Kb + kt * 32 * ROWB + k_rd[dc]);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
+        for (int qb = 0; qb < QB; ++qb) {
+          sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
+          if constexpr (SPLIT) sc.v[qb][kt] = mfma32<BF16>(af, qlo[qb][dc], sc.v[qb][kt]);
+        }
       }
     return sc;
   };
@@ -237,10 +287,167 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   // Online softmax of one tile's scores and O^T += V^T P^T.  MASK: apply the
   // causal diagonal and the end of the sequence (only on tiles that straddle
   // them).
-  auto softmax_pv = [&](auto mask_tag, Scores& sc, const uint16_t* Vs, int k0) {
+  // `issue_next` issues the score MFMAs of the following tile; it is called
+  // once on every path, inside the same basic block as this tile's
+  // exponentials, so the scheduler can interleave the two.
+  auto softmax_pv = [&](auto mask_tag, Scores& sc, const uint16_t* Vs, int k0, bool first,
+                        auto&& issue_next) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* Vb = (const char*)Vs;
     auto& s = sc.v;
+    // O^T += V^T P^T for packed probabilities pf.
+    auto pv = [&](const u32x4 (&pf)[QB][KC]) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const u32x2 lo = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB);
+          const u32x2 hi = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB + 4 * ROWB);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
+        }
+    };
+    if constexpr (!BF16) {
+      // ---- fp16: lazy reference, overflow detected from the rounded sum ----
+      if constexpr (MASK) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrow = qw0 + qb * 32 + m;
+          const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+              if (key > lim) s[qb][kt][r] = -INFINITY;
+            }
+        }
+      }
+      // p = 2^(c*s - m_run) rounded to fp16, packed as the P^T operand;
+      // tsum: this lane's sum of the rounded values.
+      auto exp_pack = [&](int qb, u32x4 (&pfq)[KC], float& tsum) {
+        const float neg_m = -m_run[qb];
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * half + 2 * e;
+              float x0, x1;
+              if constexpr (SPLIT) {
+                x0 = s[qb][kt][r];
+                x1 = s[qb][kt][r + 1];
+              } else {
+                x0 = __builtin_fmaf(s[qb][kt][r], c, neg_m);
+                x1 = __builtin_fmaf(s[qb][kt][r + 1], c, neg_m);
+              }
+              w[e] = pack2<false>(fast_exp2(x0), fast_exp2(x1));
+              if (e & 1) t1 = sum2<false>(w[e], t1); else t0 = sum2<false>(w[e], t0);
+            }
+            pfq[2 * kt + half] = w;
+          }
+        tsum = t0 + t1;
+      };
+      // Exact path: rows that need it (need[qb]: first tile, or this row's
+      // rounded sum left the safe range) raise the reference to the row max
+      // where the max exceeds it (first tile: set it to the row max) and
+      // rescale; every row then exponentiates again.  Rows that did not need
+      // it keep their reference and recompute identical values, so each row
+      // depends on its own data alone.
+      auto slow = [&](const bool (&need)[QB]) {
+        u32x4 pf[QB][KC];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+              mx0 = fmaxf(mx0, fmaxf(s[qb][kt][r], s[qb][kt][r + 1]));
+              mx1 = fmaxf(mx1, fmaxf(s[qb][kt][r + 2], s[qb][kt][r + 3]));
+            }
+          float m_new;
+          if constexpr (SPLIT) {
+            const float delta = sc.bias[qb] - m_run[qb];  // v + delta = c*s - m_run
+            const float mx = max_halves(fmaxf(mx0, mx1)) + delta;
+            m_new = first ? m_run[qb] + mx : (mx > 0.f ? m_run[qb] + mx : m_run[qb]);
+          } else {
+            const float mx = max_halves(fmaxf(mx0, mx1)) * c;
+            m_new = first ? mx : fmaxf(m_run[qb], mx);
+          }
+          if (!need[qb]) m_new = m_run[qb];
+          if (!first) {
+            const float alpha = fast_exp2(m_run[qb] - m_new);
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
+          }
+          if constexpr (SPLIT) {
+            const float shift = sc.bias[qb] - m_new;  // v + shift = c*s - m_new
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) s[qb][kt] += shift;
+          }
+          m_run[qb] = m_new;
+          float ts;
+          exp_pack(qb, pf[qb], ts);
+          l_run[qb] += ts;
+        }
+        pv(pf);
+      };
+      bool stale = first;
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) stale = stale || (__ballot(sc.bias[qb] != m_run[qb]) != 0ull);
+      }
+      if (stale) {
+        issue_next();
+        bool need[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) need[qb] = first;
+        slow(need);
+      } else {
+        // Fast path: keep the reference while the row's rounded tile sum stays
+        // at or below 2^12 (so every probability does, far from fp16
+        // overflow); a larger sum, an infinity or a new max more than 12
+        // (log2 units) above the reference takes the exact path.
+        issue_next();
+        u32x4 pf[QB][KC];
+        float ts[QB];
+        bool need[QB];
+        bool big = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          exp_pack(qb, pf[qb], ts[qb]);
+          // both halves of the wave hold parts of the same rows: decide on the
+          // row's sum so the two halves agree
+          need[qb] = !(sum_halves(ts[qb]) <= kLazyBound);
+          big = big || (__ballot(need[qb]) != 0ull);
+        }
+#if FA_FWD_SCHED_VALU > 0
+        // Interleave the next tile's score MFMAs with this tile's VALU work:
+        // operand reads first, then one MFMA per group of VALU instructions.
+        __builtin_amdgcn_sched_group_barrier(0x100, DC * KT, 0);
+#pragma unroll
+        for (int i = 0; i < QB * KT * DC * (SPLIT ? 2 : 1); ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_SCHED_VALU, 0);
+        }
+#endif
+        if (big) {
+          slow(need);
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) l_run[qb] += ts[qb];
+          pv(pf);
+        }
+      }
+      return;
+    }
+    issue_next();
     if constexpr (MASK) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -347,16 +554,21 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
     constexpr int st = decltype(stage_tag)::value;
     if (j + 3 < n_kt) issue_tile(j + 3, sK[(st + 3) % kStages], sV[(st + 3) % kStages]);
-    if (j + 1 < n_kt) nxt = compute_scores(sK[(st + 1) % kStages]);
+    // On the last tile this reads a stale (in-bounds) stage whose scores are
+    // never used; keeping it unconditional keeps it in one basic block with
+    // the exponentials.
+    auto issue_next = [&]() { nxt = compute_scores(sK[(st + 1) % kStages]); };
     const int k0 = j * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
     if (active) {
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
       if (need_mask) {
-        softmax_pv(std::true_type{}, cur, sV[st], k0);
+        softmax_pv(std::true_type{}, cur, sV[st], k0, j == 0, issue_next);
       } else {
-        softmax_pv(std::false_type{}, cur, sV[st], k0);
+        softmax_pv(std::false_type{}, cur, sV[st], k0, j == 0, issue_next);
       }
+    } else {
+      issue_next();
     }
     if (j + 3 < n_kt) {
       wait_vmem_keep<kTileLoads>();
