@@ -11,7 +11,7 @@
  * Conventions shared by every entry point
  *  - Layout: Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] with d
  *    innermost (element (b,h,i,c) at ((b*H + h)*N + i)*d + c), the layout of
- *    page 1, example 2.  LSE and the backward workspace are [B, H, N] float32.
+ *    page 1, example 2.  LSE is [B, H, N] float32.
  *  - Pointers are DEVICE pointers (HIP global memory) of the calling process's
  *    current device.  Every tensor pointer must be 16-byte aligned.
  *  - Ownership: the caller allocates and frees every buffer.  The library never
@@ -84,13 +84,14 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * per tile from Q, K and the forward's LSE.  Gradients of L = <dO, O>:
  *   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
  *   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
- * Three kernels on `stream`: D (one pass over O and dO), dK/dV (each workgroup
- * keeps a K/V tile and loops over query tiles, the loop order of that
- * section), dQ (each workgroup keeps a query tile and loops over K/V tiles).
+ * Three kernels on `stream`: D and LSE*log2(e) (one pass over O, dO and LSE),
+ * dK/dV (each workgroup keeps a K/V tile and loops over query tiles, the loop
+ * order of that section), dQ (each workgroup keeps a query tile and loops
+ * over K/V tiles).
  * No atomics: results are deterministic.
  *
  *   q, k, v, o, lse : as produced for / by flash_attn_fwd (read)
- *   dout            : [B,H,N,d] gradient of O, of O's type (read)
+ *   dout            : [B,H,N,d] gradient of O, of the input type (read)
  *   dq, dk, dv      : [B,H,N,d] of the input type (written)
  *   workspace       : device buffer of >= flash_attn_bwd_workspace_bytes(...)
  *                     bytes, 16-byte aligned, owned by the caller; its
@@ -103,7 +104,8 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int N, int d, float scale, int causal, int dtype,
                    void* stream);
 
-/* Bytes of workspace flash_attn_bwd needs (4 * B * H * N: one float per row). */
+/* Bytes of workspace flash_attn_bwd needs (8 * B * H * N: two floats per row,
+ * D and LSE*log2(e)); 0 for invalid sizes. */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Static, NUL-terminated description of a status code. */

@@ -89,7 +89,7 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None,
     """Backward: returns (dq, dk, dv) in the input dtype.
 
     ``o`` is the forward output (input dtype or float32); ``dout`` has the
-    input dtype.  The workspace (4*B*H*N bytes) is allocated here unless given.
+    input dtype.  The workspace (8*B*H*N bytes) is allocated here unless given.
     """
     torch = _torch()
     B, H, N, d = q.shape

@@ -11,16 +11,23 @@
 //   dK = scale dS^T Q,       dQ = scale dS K.
 //
 // Three kernels, all deterministic (no atomics):
-//  * bwd_pre   : D for every row (one pass over O and dO).
+//  * bwd_pre   : D and LSE*log2(e) for every row (one pass over O and dO).
 //  * bwd_dkdv  : a workgroup keeps 128 keys of K and V in registers (32 per
-//                wave) and loops over 64-row query tiles streamed through LDS
-//                (the loop order above); dK and dV accumulate in registers.
+//                wave) and loops over 64-row Q/dO tiles (the loop order
+//                above); dK and dV accumulate in registers.
 //  * bwd_dq    : a workgroup keeps 128 query rows of Q and dO in registers and
-//                loops over 64-key K/V tiles streamed through LDS.
-// All products use v_mfma_f32_32x32x16 with the same register-layout trick as
-// the forward: the 32x32 accumulator of one product is, after rounding, the
-// operand of the next, and tiles whose contraction runs over rows are stored
-// transposed in LDS so each MFMA operand is one 16-byte read.
+//                loops over 64-key K/V tiles.
+// Mapping onto CDNA4, as in the forward: v_mfma_f32_32x32x16 with the
+// accumulator of one product feeding the next as its B operand after
+// rounding; streamed tiles arrive by direct buffer->LDS loads into two
+// stages; operands that contract over tile rows are read with the
+// transposing ds_read_b64_tr_b16 from the same row-major tile (one XOR
+// swizzle serves both read patterns); the dP accumulator starts at -D so
+// the MFMA produces dP - D; tiles on the causal diagonal run a masked copy of
+// the tile body.  Rows and keys past N read as zeros and contribute nothing
+// (their dO or K/V rows are zero), and stores past N are dropped.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -29,12 +36,14 @@ namespace fa {
 constexpr int kBwdThreads = 256;
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic
+// D_i = sum_c dO_ic O_ic and LSE_i * log2(e)
 // ---------------------------------------------------------------------------
 template <int D, bool BF16, bool O_F32>
 __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __restrict__ o,
                                                               const uint16_t* __restrict__ dout,
-                                                              float* __restrict__ delta, int rows) {
+                                                              const float* __restrict__ lse,
+                                                              float* __restrict__ delta,
+                                                              float* __restrict__ lse2, int rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   constexpr int RPB = kBwdThreads / LPR;
   const int tid = threadIdx.x;
@@ -66,49 +75,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __rest
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w, 64);
-  if (row < rows && c == 0) delta[row] = acc;
-}
-
-// LDS index helpers (16-bit element units).
-template <int D>
-__device__ __forceinline__ int rm_idx(int row, int chunk) {
-  return row * D + ((chunk ^ swz_row(row)) * 8);
-}
-template <int BR>
-__device__ __forceinline__ int tr_idx(int d, int col) {
-  return d * BR + (((col >> 3) ^ swz_t(d)) * 8) + (col & 7);
-}
-
-// Write a row pair (rows 2kp, 2kp+1; 16-byte chunk c) row-major and, if
-// requested, transposed into LDS tiles of BR rows.
-template <int D, int BR, bool TRANSPOSED>
-__device__ __forceinline__ void store_pair(uint16_t* rm, uint16_t* tr, int kp, int c, u32x4 r0, u32x4 r1) {
-  const int kk = 2 * kp;
-  *(u32x4*)(&rm[rm_idx<D>(kk, c)]) = r0;
-  *(u32x4*)(&rm[rm_idx<D>(kk + 1, c)]) = r1;
-  if constexpr (TRANSPOSED) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dd = c * 8 + e;
-      const uint32_t w = (e & 1) ? hi_halves(r0[e >> 1], r1[e >> 1]) : lo_halves(r0[e >> 1], r1[e >> 1]);
-      *(uint32_t*)(&tr[tr_idx<BR>(dd, kk)]) = w;
-    }
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
   }
 }
-
-// ---------------------------------------------------------------------------
-// dK, dV: workgroup owns 128 keys (32 per wave); loop over 64-row query tiles.
-// ---------------------------------------------------------------------------
-constexpr int kDkvKeys = 128;  // keys per workgroup
-constexpr int kDkvBQ = 64;     // query rows per streamed tile
 
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse;
-  const float* delta;
+  const float* lse2;   // LSE * log2(e)
+  const float* delta;  // D
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -119,25 +98,77 @@ struct BwdArgs {
   float scale;
 };
 
+// Per-lane byte offsets shared by both kernels for a row-major LDS tile with
+// ROWB bytes per row, swizzled with swz_kq.
 template <int D>
-__host__ __device__ constexpr int dkdv_stage_elems() {
-  // sQ, sQt, sdO, sdOt (16-bit) + LSE and D rows (float, 2 x 64 -> 256 halves)
-  return 4 * kDkvBQ * D + 4 * kDkvBQ;
+struct TileOffsets {
+  static constexpr int ROWB = D * 2;
+  static constexpr int DC = D / 16;
+  static constexpr int DT = D / 32;
+  int rd[DC];  // row operand: rows 32t + perm_k(m), chunk 2dc+h (+ 32t*ROWB)
+  int tr[DT];  // transposing read for d tile dt, k-rows 8h + j (+ 16kc*ROWB, + 4r*ROWB)
+  __device__ __forceinline__ TileOffsets(int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    const int row = perm_k(m);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) rd[dc] = row * ROWB + (((2 * dc + h) ^ swz_kq(row)) * 16);
+    const int i = lane & 15, gg = (lane >> 4) & 1;
+    const int j = i >> 2, q = i & 3;
+    const int trow = 8 * h + j;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chunk = 4 * dt + 2 * (q & 1) + gg;
+      tr[dt] = trow * ROWB + ((chunk ^ swz_kq(trow)) * 16) + (q >> 1) * 8;
+    }
+  }
+};
+
+// Direct-load slot p = i*256 + tid of a tile of rows x CPR 16-byte chunks:
+// tile row p / CPR at swizzled chunk position p % CPR.
+template <int D>
+__device__ __forceinline__ uint32_t tile_src_offset(int p) {
+  constexpr int CPR = D / 8;
+  const int row = p / CPR, cpos = p % CPR;
+  return (uint32_t)(row * D * 2 + ((cpos ^ swz_kq(row)) * 16));
+}
+
+// Transposed operand (A of an O^T-shaped product) for 16 k-rows starting at
+// tile row 16*kc from the transposing reads.
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, int off, int kc, int rowb) {
+  const u32x2 lo = lds_read_tr16(tile + off + kc * 16 * rowb);
+  const u32x2 hi = lds_read_tr16(tile + off + kc * 16 * rowb + 4 * rowb);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+template <int D>
+constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup owns 128 keys (32 per wave); loop over 64-row query tiles.
+// ---------------------------------------------------------------------------
+constexpr int kDkvKeys = 128;  // keys per workgroup
+constexpr int kDkvBQ = 64;     // query rows per streamed tile
+
+template <int D>
+__host__ __device__ constexpr int dkdv_stage_bytes() {
+  return 2 * kDkvBQ * D * 2 + 2 * kDkvBQ * 4;  // Q, dO tiles + LSE2, D rows
 }
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BQ = kDkvBQ;
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
-  constexpr int QT = BQ / 32;  // 32-row query tiles per streamed tile
+  constexpr int QT = BQ / 32;  // 32-row query sub-tiles per streamed tile
   constexpr int QC = BQ / 16;  // 16-row query chunks (contraction of dK, dV)
   constexpr int CPR = D / 8;
-  constexpr int PAIRS = (BQ / 2) * CPR / kBwdThreads;  // row pairs per thread per tensor
-  static_assert(PAIRS * kBwdThreads == (BQ / 2) * CPR, "tile split");
-  constexpr int STAGE = dkdv_stage_elems<D>();
+  constexpr int ROWB = D * 2;
+  constexpr int LOADS = BQ * CPR / kBwdThreads;
+  static_assert(LOADS * kBwdThreads == BQ * CPR, "tile split");
+  constexpr int STAGE = dkdv_stage_bytes<D>();
+  constexpr int TILE = BQ * ROWB;
 
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 31, h = lane >> 5;
@@ -157,25 +188,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
   const int N = a.N;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Qg = a.q + base;
-  const uint16_t* __restrict__ dOg = a.dout + base;
-  const float* __restrict__ Lg = a.lse + (size_t)bh * N;
-  const float* __restrict__ Dg = a.delta + (size_t)bh * N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
+  const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
+  const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
+  const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
   const int kw0 = kvt * kDkvKeys + wave * 32;  // first key of this wave
   const int key = kw0 + m;                     // this lane's key (column of S)
 
-  // K and V fragments as B operands (lane: key m; slot i: d = 16dc + 8h + i).
+  // K and V as B operands (lane: key m; slot i: d = 16dc + 8h + i).
   u32x4 kf[DC], vf[DC];
+  {
+    const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
+    const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    if (key < N) {
-      kf[dc] = *(const u32x4*)(a.k + base + (size_t)key * D + dc * 16 + 8 * h);
-      vf[dc] = *(const u32x4*)(a.v + base + (size_t)key * D + dc * 16 + 8 * h);
-    } else {
-      kf[dc] = u32x4{0, 0, 0, 0};
-      vf[dc] = u32x4{0, 0, 0, 0};
+    for (int dc = 0; dc < DC; ++dc) {
+      const uint32_t off = (uint32_t)((key * D + dc * 16 + 8 * h) * 2);
+      kf[dc] = bload16(rk, off, 0);
+      vf[dc] = bload16(rv, off, 0);
     }
   }
+  const TileOffsets<D> to(lane);
+  uint32_t src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) src[i] = tile_src_offset<D>(i * kBwdThreads + tid);
 
   f32x16 dkt[DT], dvt[DT];
 #pragma unroll
@@ -187,148 +223,134 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_qt = (N + BQ - 1) / BQ;
   const int qt_begin = CAUSAL ? (kvt * kDkvKeys) / BQ : 0;
 
-  u32x4 qreg[PAIRS][2], oreg[PAIRS][2];
-  float lreg = 0.f;  // threads 0..63: LSE*log2e of one row; 64..127: D of one row
-
-  auto load_tile = [&](int qt) {
-    const int q0 = qt * BQ;
+  auto issue_tile = [&](int qt, char* stage) {
+    const uint32_t soff = (uint32_t)(qt * BQ * ROWB);
 #pragma unroll
-    for (int i = 0; i < PAIRS; ++i) {
-      const int p = tid + i * kBwdThreads;
-      const int c = p % CPR, kp = p / CPR;
-      const int r = q0 + 2 * kp;
-      qreg[i][0] = r < N ? *(const u32x4*)(Qg + (size_t)r * D + c * 8) : u32x4{0, 0, 0, 0};
-      qreg[i][1] = r + 1 < N ? *(const u32x4*)(Qg + (size_t)(r + 1) * D + c * 8) : u32x4{0, 0, 0, 0};
-      oreg[i][0] = r < N ? *(const u32x4*)(dOg + (size_t)r * D + c * 8) : u32x4{0, 0, 0, 0};
-      oreg[i][1] = r + 1 < N ? *(const u32x4*)(dOg + (size_t)(r + 1) * D + c * 8) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (i * kBwdThreads + wave * 64) * 16;
+      bload16_lds(rq, stage + slot, src[i], soff);
+      bload16_lds(rg, stage + TILE + slot, src[i], soff);
     }
-    if (tid < BQ) {
-      const int r = q0 + tid;
-      lreg = r < N ? Lg[r] * kLog2e : INFINITY;  // padded rows: P = exp2(-inf) = 0
-    } else if (tid < 2 * BQ) {
-      const int r = q0 + tid - BQ;
-      lreg = r < N ? Dg[r] : 0.f;
+    // 64 LSE2 and 64 D values: 16 lanes of waves 0 and 1.
+    if (lane < 16) {
+      if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
+      if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
     }
   };
-  auto store_tile = [&](int st) {
-    uint16_t* sQ = smem + st * STAGE;
-    uint16_t* sQt = sQ + BQ * D;
-    uint16_t* sdO = sQt + BQ * D;
-    uint16_t* sdOt = sdO + BQ * D;
-    float* sL = (float*)(sdOt + BQ * D);
-#pragma unroll
-    for (int i = 0; i < PAIRS; ++i) {
-      const int p = tid + i * kBwdThreads;
-      const int c = p % CPR, kp = p / CPR;
-      store_pair<D, BQ, true>(sQ, sQt, kp, c, qreg[i][0], qreg[i][1]);
-      store_pair<D, BQ, true>(sdO, sdOt, kp, c, oreg[i][0], oreg[i][1]);
-    }
-    if (tid < 2 * BQ) sL[tid] = lreg;
-  };
-
-  if (qt_begin < n_qt) {
-    load_tile(qt_begin);
-    store_tile(0);
-  }
-  __syncthreads();
 
   const float c = a.c;
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    const int st = (qt - qt_begin) & 1;
-    if (qt + 1 < n_qt) load_tile(qt + 1);
+  auto tile_body = [&](auto mask_tag, const char* stage, int q0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* sQ = stage;
+    const char* sG = stage + TILE;
+    const float* sL = (const float*)(stage + 2 * TILE);
+    const float* sD = sL + BQ;
+    // S = Q K^T; dP - D = dO V^T - D (rows: queries with perm_k, cols: keys).
+    // Register r of sub-tile t holds query row t*32 + 16(r/8) + 8h + r%8.
+    f32x16 s[QT], dp[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int qb = t * 32 + 16 * g + 8 * h;
+        const f32x4 d0 = *(const f32x4*)(&sD[qb]);
+        const f32x4 d1 = *(const f32x4*)(&sD[qb + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dp[t][8 * g + e] = -d0[e];
+          dp[t][8 * g + 4 + e] = -d1[e];
+        }
+      }
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const u32x4 qa = *(const u32x4*)(sQ + t * 32 * ROWB + to.rd[dc]);
+        const u32x4 ga = *(const u32x4*)(sG + t * 32 * ROWB + to.rd[dc]);
+        s[t] = mfma32<BF16>(qa, kf[dc], s[t]);
+        dp[t] = mfma32<BF16>(ga, vf[dc], dp[t]);
+      }
+    }
+    u32x4 pp[QC], ps[QC];
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int qb = t * 32 + 16 * g + 8 * h;
+        const f32x4 l0 = *(const f32x4*)(&sL[qb]);
+        const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float l2 = e < 4 ? l0[e] : l1[e - 4];
+          float p = fast_exp2(__builtin_fmaf(s[t][8 * g + e], c, -l2));
+          if constexpr (MASK) {
+            if (key > q0 + qb + e) p = 0.f;
+          }
+          pv[e] = p;
+          dsv[e] = p * dp[t][8 * g + e];
+        }
+        u32x4 wp, wd;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wp[e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
+          wd[e] = pack2<BF16>(dsv[2 * e], dsv[2 * e + 1]);
+        }
+        pp[2 * t + g] = wp;
+        ps[2 * t + g] = wd;
+      }
+    // dV^T += dO^T P ; dK^T += Q^T dS   (rows: d with perm_o, cols: keys)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int qc = 0; qc < QC; ++qc) {
+        const u32x4 ga = tr_operand(sG, to.tr[dt], qc, ROWB);
+        const u32x4 qa = tr_operand(sQ, to.tr[dt], qc, ROWB);
+        dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
+        dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
+      }
+  };
+
+  auto iteration = [&](int qt, char* cur, char* nxt) {
+    if (qt + 1 < n_qt) issue_tile(qt + 1, nxt);
     const int q0 = qt * BQ;
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
     if (active) {
-      const uint16_t* sQ = smem + st * STAGE;
-      const uint16_t* sQt = sQ + BQ * D;
-      const uint16_t* sdO = sQt + BQ * D;
-      const uint16_t* sdOt = sdO + BQ * D;
-      const float* sL = (const float*)(sdOt + BQ * D);
-      const float* sD = sL + BQ;
-
-      // S = Q K^T and dP = dO V^T (rows: queries with perm_k, cols: keys)
-      f32x16 s[QT], dp[QT];
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-        s[t] = f32x16{};
-        dp[t] = f32x16{};
-        const int row = t * 32 + perm_k(m);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 qa = *(const u32x4*)(&sQ[rm_idx<D>(row, 2 * dc + h)]);
-          const u32x4 ga = *(const u32x4*)(&sdO[rm_idx<D>(row, 2 * dc + h)]);
-          s[t] = mfma32<BF16>(qa, kf[dc], s[t]);
-          dp[t] = mfma32<BF16>(ga, vf[dc], dp[t]);
-        }
-      }
-      const bool need_mask = (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31);
-      u32x4 pp[QC], ps[QC];
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          // register r = 8g + e  <->  query row t*32 + 16g + 8h + e of the tile
-          const int qb = t * 32 + 16 * g + 8 * h;
-          const f32x4 l0 = *(const f32x4*)(&sL[qb]);
-          const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
-          const f32x4 d0 = *(const f32x4*)(&sD[qb]);
-          const f32x4 d1 = *(const f32x4*)(&sD[qb + 4]);
-          float pv[8], dsv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float lse2 = e < 4 ? l0[e] : l1[e - 4];
-            const float dd = e < 4 ? d0[e] : d1[e - 4];
-            float p = fast_exp2(__builtin_fmaf(s[t][8 * g + e], c, -lse2));
-            if (need_mask) {
-              const int qrow = q0 + qb + e;
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            pv[e] = p;
-            dsv[e] = p * (dp[t][8 * g + e] - dd);
-          }
-          u32x4 wp, wd;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            wp[e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
-            wd[e] = pack2<BF16>(dsv[2 * e], dsv[2 * e + 1]);
-          }
-          pp[2 * t + g] = wp;
-          ps[2 * t + g] = wd;
-        }
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (rows: d with perm_o, cols: keys)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int drow = dt * 32 + perm_o(m);
-#pragma unroll
-        for (int qc = 0; qc < QC; ++qc) {
-          const int col = 16 * qc + 8 * h;
-          const u32x4 ga = *(const u32x4*)(&sdOt[tr_idx<BQ>(drow, col)]);
-          const u32x4 qa = *(const u32x4*)(&sQt[tr_idx<BQ>(drow, col)]);
-          dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
-          dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
-        }
+      if (CAUSAL && q0 < kw0 + 31) {
+        tile_body(std::true_type{}, cur, q0);
+      } else {
+        tile_body(std::false_type{}, cur, q0);
       }
     }
-    if (qt + 1 < n_qt) store_tile(st ^ 1);
+    wait_vmem();
     __syncthreads();
+  };
+
+  char* st0 = smem;
+  char* st1 = smem + STAGE;
+  if (qt_begin < n_qt) issue_tile(qt_begin, st0);
+  wait_vmem();
+  __syncthreads();
+  for (int qt = qt_begin; qt < n_qt; qt += 2) {
+    iteration(qt, st0, st1);
+    if (qt + 1 < n_qt) iteration(qt + 1, st1, st0);
   }
 
-  if (key < N) {
+  // dK = scale dS^T Q, dV: lane (key m, half h) holds d = 32dt + 16h + r.
+  const brsrc_t rdk = make_rsrc(a.dk + base, head_bytes);
+  const brsrc_t rdv = make_rsrc(a.dv + base, head_bytes);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const size_t off = base + (size_t)key * D + dt * 32 + 16 * h;
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint32_t off = (uint32_t)((key * D + dt * 32 + 16 * h) * 2);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4 wk, wv;
+    for (int e = 0; e < 2; ++e) {
+      u32x4 wk, wv;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          wk[t] = pack2<BF16>(dkt[dt][8 * e + 2 * t] * a.scale, dkt[dt][8 * e + 2 * t + 1] * a.scale);
-          wv[t] = pack2<BF16>(dvt[dt][8 * e + 2 * t], dvt[dt][8 * e + 2 * t + 1]);
-        }
-        *(u32x4*)(a.dk + off + 8 * e) = wk;
-        *(u32x4*)(a.dv + off + 8 * e) = wv;
+      for (int t = 0; t < 4; ++t) {
+        wk[t] = pack2<BF16>(dkt[dt][8 * e + 2 * t] * a.scale, dkt[dt][8 * e + 2 * t + 1] * a.scale);
+        wv[t] = pack2<BF16>(dvt[dt][8 * e + 2 * t], dvt[dt][8 * e + 2 * t + 1]);
       }
+      bstore16(wk, rdk, off + 16 * e, 0);
+      bstore16(wv, rdv, off + 16 * e, 0);
     }
   }
 }
@@ -340,23 +362,25 @@ constexpr int kDqRows = 128;
 constexpr int kDqBK = 64;
 
 template <int D>
-__host__ __device__ constexpr int dq_stage_elems() {
-  return 3 * kDqBK * D;  // sK, sKt, sV
+__host__ __device__ constexpr int dq_stage_bytes() {
+  return 2 * kDqBK * D * 2;  // K, V tiles
 }
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BK = kDqBK;
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int KT = BK / 32;
   constexpr int KC = BK / 16;
   constexpr int CPR = D / 8;
-  constexpr int PAIRS = (BK / 2) * CPR / kBwdThreads;
-  static_assert(PAIRS * kBwdThreads == (BK / 2) * CPR, "tile split");
-  constexpr int STAGE = dq_stage_elems<D>();
+  constexpr int ROWB = D * 2;
+  constexpr int LOADS = BK * CPR / kBwdThreads;
+  static_assert(LOADS * kBwdThreads == BK * CPR, "tile split");
+  constexpr int STAGE = dq_stage_bytes<D>();
+  constexpr int TILE = BK * ROWB;
 
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 31, h = lane >> 5;
@@ -376,24 +400,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   }
   const int N = a.N;
   const size_t base = (size_t)bh * N * D;
-  const uint16_t* __restrict__ Kg = a.k + base;
-  const uint16_t* __restrict__ Vg = a.v + base;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
+  const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
   const int qw0 = qt * kDqRows + wave * 32;
   const int qrow = qw0 + m;
 
+  // Q^T and dO^T as B operands (lane: query m; slot i: d = 16dc + 8h + i).
   u32x4 qf[DC], gf[DC];
+  {
+    const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
+    const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
 #pragma unroll
-  for (int dc = 0; dc < DC; ++dc) {
-    if (qrow < N) {
-      qf[dc] = *(const u32x4*)(a.q + base + (size_t)qrow * D + dc * 16 + 8 * h);
-      gf[dc] = *(const u32x4*)(a.dout + base + (size_t)qrow * D + dc * 16 + 8 * h);
-    } else {
-      qf[dc] = u32x4{0, 0, 0, 0};
-      gf[dc] = u32x4{0, 0, 0, 0};
+    for (int dc = 0; dc < DC; ++dc) {
+      const uint32_t off = (uint32_t)((qrow * D + dc * 16 + 8 * h) * 2);
+      qf[dc] = bload16(rq, off, 0);
+      gf[dc] = bload16(rg, off, 0);
     }
   }
-  const float lse2 = qrow < N ? a.lse[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dl = qrow < N ? a.delta[(size_t)bh * N + qrow] : 0.f;
+  // Rows past N: LSE2 and D read as 0; their Q and dO rows are 0 and dQ is
+  // not stored.
+  float lse2, dl;
+  {
+    const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
+    const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
+    lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
+    dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
+  }
+  const TileOffsets<D> to(lane);
+  uint32_t src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) src[i] = tile_src_offset<D>(i * kBwdThreads + tid);
 
   f32x16 dqt[DT];
 #pragma unroll
@@ -402,111 +439,104 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(BwdArgs a) {
   const int kend = CAUSAL ? min(N, qt * kDqRows + kDqRows) : N;
   const int n_kt = (kend + BK - 1) / BK;
 
-  u32x4 kreg[PAIRS][2], vreg[PAIRS][2];
-  auto load_tile = [&](int j) {
-    const int k0 = j * BK;
+  auto issue_tile = [&](int j, char* stage) {
+    const uint32_t soff = (uint32_t)(j * BK * ROWB);
 #pragma unroll
-    for (int i = 0; i < PAIRS; ++i) {
-      const int p = tid + i * kBwdThreads;
-      const int c = p % CPR, kp = p / CPR;
-      const int r = k0 + 2 * kp;
-      kreg[i][0] = r < N ? *(const u32x4*)(Kg + (size_t)r * D + c * 8) : u32x4{0, 0, 0, 0};
-      kreg[i][1] = r + 1 < N ? *(const u32x4*)(Kg + (size_t)(r + 1) * D + c * 8) : u32x4{0, 0, 0, 0};
-      vreg[i][0] = r < N ? *(const u32x4*)(Vg + (size_t)r * D + c * 8) : u32x4{0, 0, 0, 0};
-      vreg[i][1] = r + 1 < N ? *(const u32x4*)(Vg + (size_t)(r + 1) * D + c * 8) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (i * kBwdThreads + wave * 64) * 16;
+      bload16_lds(rk, stage + slot, src[i], soff);
+      bload16_lds(rv, stage + TILE + slot, src[i], soff);
     }
   };
-  auto store_tile = [&](int st) {
-    uint16_t* sK = smem + st * STAGE;
-    uint16_t* sKt = sK + BK * D;
-    uint16_t* sV = sKt + BK * D;
-#pragma unroll
-    for (int i = 0; i < PAIRS; ++i) {
-      const int p = tid + i * kBwdThreads;
-      const int c = p % CPR, kp = p / CPR;
-      store_pair<D, BK, true>(sK, sKt, kp, c, kreg[i][0], kreg[i][1]);
-      store_pair<D, BK, false>(sV, nullptr, kp, c, vreg[i][0], vreg[i][1]);
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
 
   const float c = a.c;
-  for (int j = 0; j < n_kt; ++j) {
-    const int st = j & 1;
-    if (j + 1 < n_kt) load_tile(j + 1);
+  auto tile_body = [&](auto mask_tag, const char* stage, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* sK = stage;
+    const char* sV = stage + TILE;
+    // S^T = K Q^T, dP^T - D = V dO^T - D (rows: keys with perm_k, cols:
+    // queries).  Register r of key tile kt holds key kt*32 + 16(r/8) + 8h + r%8.
+    f32x16 s[KT], dp[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[kt][r] = -dl;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        const u32x4 ka = *(const u32x4*)(sK + kt * 32 * ROWB + to.rd[dc]);
+        const u32x4 va = *(const u32x4*)(sV + kt * 32 * ROWB + to.rd[dc]);
+        s[kt] = mfma32<BF16>(ka, qf[dc], s[kt]);
+        dp[kt] = mfma32<BF16>(va, gf[dc], dp[kt]);
+      }
+    }
+    u32x4 ps[KC];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(__builtin_fmaf(s[kt][r], c, -lse2));
+        if constexpr (MASK) {
+          const int keyi = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
+          if (keyi > qrow) p = 0.f;
+        }
+        dsv[r] = p * dp[kt][r];
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack2<BF16>(dsv[8 * g + 2 * e], dsv[8 * g + 2 * e + 1]);
+        ps[2 * kt + g] = w;
+      }
+    }
+    // dQ^T += K^T dS^T (rows: d with perm_o, cols: queries)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const u32x4 ka = tr_operand(sK, to.tr[dt], kc, ROWB);
+        dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
+      }
+  };
+
+  auto iteration = [&](int j, char* cur, char* nxt) {
+    if (j + 1 < n_kt) issue_tile(j + 1, nxt);
     const int k0 = j * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 31);
     if (active) {
-      const uint16_t* sK = smem + st * STAGE;
-      const uint16_t* sKt = sK + BK * D;
-      const uint16_t* sV = sKt + BK * D;
-      // S^T = K Q^T, dP^T = V dO^T (rows: keys with perm_k, cols: queries)
-      f32x16 s[KT], dp[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        s[kt] = f32x16{};
-        dp[kt] = f32x16{};
-        const int row = kt * 32 + perm_k(m);
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc) {
-          const u32x4 ka = *(const u32x4*)(&sK[rm_idx<D>(row, 2 * dc + h)]);
-          const u32x4 va = *(const u32x4*)(&sV[rm_idx<D>(row, 2 * dc + h)]);
-          s[kt] = mfma32<BF16>(ka, qf[dc], s[kt]);
-          dp[kt] = mfma32<BF16>(va, gf[dc], dp[kt]);
-        }
-      }
-      const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
-      u32x4 ps[KC];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        float dsv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[kt][r], c, -lse2));
-          if (need_mask) {
-            const int key = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-            if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-          }
-          dsv[r] = p * (dp[kt][r] - dl);
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack2<BF16>(dsv[8 * g + 2 * e], dsv[8 * g + 2 * e + 1]);
-          ps[2 * kt + g] = w;
-        }
-      }
-      // dQ^T += K^T dS^T (rows: d with perm_o, cols: queries)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int drow = dt * 32 + perm_o(m);
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const u32x4 ka = *(const u32x4*)(&sKt[tr_idx<BK>(drow, 16 * kc + 8 * h)]);
-          dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
-        }
+      if (CAUSAL && k0 + BK - 1 > qw0) {
+        tile_body(std::true_type{}, cur, k0);
+      } else {
+        tile_body(std::false_type{}, cur, k0);
       }
     }
-    if (j + 1 < n_kt) store_tile(st ^ 1);
+    wait_vmem();
     __syncthreads();
+  };
+
+  char* st0 = smem;
+  char* st1 = smem + STAGE;
+  issue_tile(0, st0);
+  wait_vmem();
+  __syncthreads();
+  for (int j = 0; j < n_kt; j += 2) {
+    iteration(j, st0, st1);
+    if (j + 1 < n_kt) iteration(j + 1, st1, st0);
   }
 
-  if (qrow < N) {
+  const brsrc_t rdq = make_rsrc(a.dq + base, head_bytes);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const size_t off = base + (size_t)qrow * D + dt * 32 + 16 * h;
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint32_t off = (uint32_t)((qrow * D + dt * 32 + 16 * h) * 2);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        u32x4 w;
+    for (int e = 0; e < 2; ++e) {
+      u32x4 w;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          w[t] = pack2<BF16>(dqt[dt][8 * e + 2 * t] * a.scale, dqt[dt][8 * e + 2 * t + 1] * a.scale);
-        *(u32x4*)(a.dq + off + 8 * e) = w;
-      }
+      for (int t = 0; t < 4; ++t)
+        w[t] = pack2<BF16>(dqt[dt][8 * e + 2 * t] * a.scale, dqt[dt][8 * e + 2 * t + 1] * a.scale);
+      bstore16(w, rdq, off + 16 * e, 0);
     }
   }
 }
@@ -526,7 +556,7 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
     constexpr int RPB = kBwdThreads / (D / 8);
     const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     hipLaunchKernelGGL((bwd_pre_kernel<D, BF16, O_F32>), grid, dim3(kBwdThreads), 0, stream, p.o,
-                       (const uint16_t*)p.dout, p.delta, rows);
+                       (const uint16_t*)p.dout, p.lse, p.delta, p.lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -535,7 +565,7 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   a.k = (const uint16_t*)p.k;
   a.v = (const uint16_t*)p.v;
   a.dout = (const uint16_t*)p.dout;
-  a.lse = p.lse;
+  a.lse2 = p.lse2;
   a.delta = p.delta;
   a.dq = (uint16_t*)p.dq;
   a.dk = (uint16_t*)p.dk;
@@ -546,7 +576,7 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   a.scale = p.scale;
   {
     a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
-    const int lds = 2 * dkdv_stage_elems<D>() * 2;
+    const int lds = 2 * dkdv_stage_bytes<D>();
     auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -556,7 +586,7 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   }
   {
     a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
-    const int lds = 2 * dq_stage_elems<D>() * 2;
+    const int lds = 2 * dq_stage_bytes<D>();
     auto kern = bwd_dq_kernel<D, BF16, CAUSAL>;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;

@@ -157,6 +157,11 @@ __device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 3) & 1)
 // Row-major V tile read through lds_read_tr16: rows 4 apart share a bank
 // window, so chunks are XORed with s(row % 4) in {0, 1, 4, 5}.
 __device__ __forceinline__ int swz_v(int r) { return (r & 1) | ((r & 2) << 1); }
+// Row-major tile read both ways: as a row operand (8 lanes on rows
+// perm_k(m), one chunk) and through lds_read_tr16 (16 lanes on rows 4 apart
+// in pairs of chunks c, c^2).  Bits 0 and 2 of the XOR follow row % 4 and
+// bit 1 follows bit 3 of the row, which keeps both patterns conflict-free.
+__device__ __forceinline__ int swz_kq(int r) { return (r & 1) | ((r & 2) << 1) | (((r >> 3) & 1) << 1); }
 // Transposed [d][keys] tile: distinct over the rows perm_o(m) of 8 lanes and
 // over rows 8*c + i (c = 0..7) written by 8 lanes.
 __device__ __forceinline__ int swz_t(int d) {

@@ -51,7 +51,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (B < 1 || H < 1 || N < 1) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -77,6 +77,7 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.dk = dk;
   p.dv = dv;
   p.delta = (float*)workspace;
+  p.lse2 = (float*)workspace + (size_t)B * H * N;
   p.BH = B * H;
   p.N = N;
   p.d = d;

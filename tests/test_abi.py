@@ -47,7 +47,7 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.flash_attn_bwd_workspace_bytes(2, 12, 4096, 64) == 4 * 2 * 12 * 4096
+    assert lib.flash_attn_bwd_workspace_bytes(2, 12, 4096, 64) == 8 * 2 * 12 * 4096
     assert lib.flash_attn_bwd_workspace_bytes(0, 1, 1, 64) == 0
 
 
@@ -88,7 +88,7 @@ def test_fwd_validation(lib, kw, status):
     (dict(dout=None), 1), (dict(dv=None), 1),
     (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=7), 4),
     (dict(dq=P + 8), 5), (dict(workspace=P + 8), 5),
-    (dict(workspace=None), 7), (dict(workspace_bytes=4 * 8 - 1), 7),
+    (dict(workspace=None), 7), (dict(workspace_bytes=8 * 8 - 1), 7),
     (dict(scale=-1.0), 8),
 ])
 def test_bwd_validation(lib, kw, status):
