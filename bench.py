@@ -22,8 +22,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 MFMA peak
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "fwd_traffic.json")
-FWD_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp"]
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic_B2H12N8192d64_f16.json")
+KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hip", "io_aware_exact_08_amd/csrc/fa_bwd.hip",
+                  "io_aware_exact_08_amd/csrc/fa_device.hpp"]
 
 
 def parse():
@@ -46,15 +47,16 @@ def parse():
 
 def sources_digest():
     h = hashlib.sha256()
-    for rel in FWD_SOURCES:
+    for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(per_launch_bytes_algo):
-    """HBM bytes per forward launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on different kernel sources."""
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` (fetch + write, copy-calibrated) from the
+    committed rocprofv3 counter summary, or None when it is missing or was
+    taken on different kernel sources."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
@@ -62,7 +64,7 @@ def traffic_from_profile(per_launch_bytes_algo):
         return None
     if rec.get("sources_sha256_16") != sources_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch", {}).get(kernel)
 
 
 def cpu_baseline(w, heads):
@@ -119,17 +121,22 @@ def main():
     ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    # One step: forward, then the backward's three stages (exactly what
+    # flash_attn_bwd enqueues), with events between the kernels.
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, o=o, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
-        if not args.fwd_only:
-            fa.flash_attn_bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale,
-                              dq=dq, dk=dk, dv=dv, workspace=ws)
+        def mark(i):
             if ev is not None:
-                ev[2].record(stream)
+                ev[i].record(stream)
+        mark(0)
+        fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        mark(1)
+        if not args.fwd_only:
+            fa.flash_attn_bwd_preprocess(o, lse, do, ws)
+            mark(2)
+            fa.flash_attn_bwd_dkdv(q, k, v, do, ws, causal=w.causal, scale=w.scale, dk=dk, dv=dv)
+            mark(3)
+            fa.flash_attn_bwd_dq(q, k, v, do, ws, causal=w.causal, scale=w.scale, dq=dq)
+            mark(4)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -143,22 +150,24 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [] if args.fwd_only else [e[1].elapsed_time(e[2]) for e in events]
+    def avg_ms(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
+
     ms_per_step = wall * 1e3 / args.steps
     causal_f = 0.5 if w.causal else 1.0
-    fwd_flops = 4.0 * B * H * N * N * d * causal_f
-    bwd_flops = 2.5 * fwd_flops
+    unit = B * H * N * N * d * causal_f  # N^2 d per head, summed over heads
+    fwd_flops = 4.0 * unit
+    bwd_flops = 2.5 * fwd_flops  # the metric's credit for the backward
     step_flops = fwd_flops + (0.0 if args.fwd_only else bwd_flops)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    fwd_avg = float(np.mean(fwd_ms))
+    fwd_avg = avg_ms(0, 1)
     fwd_tflops = fwd_flops / (fwd_avg * 1e-3) / 1e12
     res = {
         "metric": "attention fwd(+bwd) TFLOP/s on 1 MI355X and % of MFMA peak, B=2 H=12 d=64",
@@ -184,18 +193,32 @@ def main():
         "fwd": {"ms": round(fwd_avg, 4), "tflops": round(fwd_tflops, 2),
                 "frac_of_peak": round(fwd_tflops / PEAK_MFMA_F16_TFLOPS, 4)},
     }
-    if bwd_ms:
-        bwd_avg = float(np.mean(bwd_ms))
+    # Per-kernel event timings; algorithmic flops per launch are 2*N^2*d per
+    # head for every product the kernel computes (forward 2, dK/dV 4, dQ 3).
+    kernels = {"fwd_kernel": (fwd_avg, 4.0 * unit)}
+    if not args.fwd_only:
+        pre_ms, dkdv_ms, dq_ms = avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
+        bwd_avg = pre_ms + dkdv_ms + dq_ms
         res["bwd"] = {"ms": round(bwd_avg, 4),
                       "tflops_credited": round(bwd_flops / (bwd_avg * 1e-3) / 1e12, 2),
                       "kernels": "bwd_pre + bwd_dkdv + bwd_dq"}
-    # Roofline of the forward kernel: algorithmic flops per launch over its
-    # average event-timed duration in the timed region.
+        kernels.update({"bwd_dkdv_kernel": (dkdv_ms, 8.0 * unit),
+                        "bwd_dq_kernel": (dq_ms, 6.0 * unit)})
+        pre_bytes = B * H * N * (2 * d * 2 + 4 + 8)  # read O, dO, LSE; write D, LSE2
+        res["bwd_pre"] = {"ms": round(pre_ms, 4),
+                          "GB_per_s": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1)}
+    res["kernels"] = {k_: {"ms": round(t, 4), "algorithmic_tflops": round(fl / (t * 1e-3) / 1e12, 2),
+                           "frac_of_peak": round(fl / (t * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
+                      for k_, (t, fl) in kernels.items()}
+    # Roofline of the dominant (longest) kernel.
+    dom = max(kernels, key=lambda k_: kernels[k_][0])
+    t_dom, fl_dom = kernels[dom]
+    ach = fl_dom / (t_dom * 1e-3) / 1e12
     res["roofline"] = {
-        "kernel": "fwd_kernel<64,f16,non-causal>" if not w.causal else "fwd_kernel<64,f16,causal>",
-        "bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_MFMA_F16_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_MFMA_F16_TFLOPS, 4),
-        "traffic": traffic_from_profile(None),
+        "kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+        "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4),
+        "traffic": traffic_from_profile(dom),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)

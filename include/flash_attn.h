@@ -104,6 +104,32 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int N, int d, float scale, int causal, int dtype,
                    void* stream);
 
+/*
+ * The three stages of flash_attn_bwd, callable on their own (same arguments,
+ * layouts and checks as flash_attn_bwd; flash_attn_bwd is exactly these three
+ * in order on one stream).  dK/dV and dQ only read the workspace the
+ * preprocess wrote, so once it has run they may run on different streams.
+ *
+ * flash_attn_bwd_preprocess: D_i = sum_c dO_ic O_ic and LSE_i*log2(e) into the
+ *   workspace (page 2, "Re-computation": the per-row terms the recompute needs).
+ *   `dtype` selects the input type and O's type as for the forward.
+ * flash_attn_bwd_dkdv: dK and dV.  Each workgroup keeps a K/V tile and loops
+ *   over query tiles, the loop order of that section.
+ * flash_attn_bwd_dq: dQ.  Each workgroup keeps a query tile and loops over
+ *   K/V tiles.
+ */
+int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int H, int N, int d, int dtype, void* stream);
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal, int dtype,
+                        void* stream);
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const void* workspace, size_t workspace_bytes, void* dq,
+                      int B, int H, int N, int d, float scale, int causal, int dtype,
+                      void* stream);
+
 /* Bytes of workspace flash_attn_bwd needs (8 * B * H * N: two floats per row,
  * D and LSE*log2(e)); 0 for invalid sizes. */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);

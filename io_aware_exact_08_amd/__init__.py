@@ -15,7 +15,8 @@ import math
 from . import _lib
 from ._lib import FlashAttnError, status_string  # noqa: F401
 
-__all__ = ["flash_attn_fwd", "flash_attn_bwd", "FlashAttnError", "status_string",
+__all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+           "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "FlashAttnError", "status_string",
            "dtype_code", "workspace_bytes"]
 
 
@@ -118,3 +119,69 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None,
     if st != _lib.FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd")
     return dq, dk, dv
+
+
+def _bwd_common(q, k, v, dout):
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    return B, H, N, d
+
+
+def _check_ws(workspace, B, H, N, d):
+    torch = _torch()
+    if not workspace.is_cuda or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 device tensor")
+    if workspace.numel() * 4 < workspace_bytes(B, H, N, d):
+        raise ValueError("workspace too small")
+
+
+def flash_attn_bwd_preprocess(o, lse, dout, workspace, in_dtype=None):
+    """Stage 1 of the backward: D and LSE*log2(e) into `workspace`."""
+    torch = _torch()
+    B, H, N, d = dout.shape
+    in_dtype = dout.dtype if in_dtype is None else in_dtype
+    _check(dout, "dout", (B, H, N, d), in_dtype)
+    _check(o, "o", (B, H, N, d), o.dtype)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    _check_ws(workspace, B, H, N, d)
+    code = dtype_code(in_dtype, o.dtype == torch.float32)
+    st = _lib.flash_attn_bwd_preprocess(o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel() * 4,
+                                        B, H, N, d, code, _stream(dout))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_preprocess")
+
+
+def flash_attn_bwd_dkdv(q, k, v, dout, workspace, causal=False, scale=None, dk=None, dv=None):
+    """Stage 2 of the backward: dK, dV (needs the preprocessed workspace)."""
+    B, H, N, d = _bwd_common(q, k, v, dout)
+    _check_ws(workspace, B, H, N, d)
+    dk = _torch().empty_like(k) if dk is None else dk
+    dv = _torch().empty_like(v) if dv is None else dv
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * 4, dk.data_ptr(),
+                                  dv.data_ptr(), B, H, N, d, sc, int(bool(causal)),
+                                  dtype_code(q.dtype, False), _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_dkdv")
+    return dk, dv
+
+
+def flash_attn_bwd_dq(q, k, v, dout, workspace, causal=False, scale=None, dq=None):
+    """Stage 3 of the backward: dQ (needs the preprocessed workspace)."""
+    B, H, N, d = _bwd_common(q, k, v, dout)
+    _check_ws(workspace, B, H, N, d)
+    dq = _torch().empty_like(q) if dq is None else dq
+    _check(dq, "dq", (B, H, N, d), q.dtype)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                workspace.data_ptr(), workspace.numel() * 4, dq.data_ptr(),
+                                B, H, N, d, sc, int(bool(causal)), dtype_code(q.dtype, False),
+                                _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_dq")
+    return dq

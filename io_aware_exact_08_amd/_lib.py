@@ -18,6 +18,9 @@ FA_F16, FA_BF16, FA_F16_OUT_F32, FA_BF16_OUT_F32 = 0, 1, 2, 3
 EXPORTED = (
     "flash_attn_fwd",
     "flash_attn_bwd",
+    "flash_attn_bwd_preprocess",
+    "flash_attn_bwd_dkdv",
+    "flash_attn_bwd_dq",
     "flash_attn_bwd_workspace_bytes",
     "flash_attn_status_string",
     "flash_attn_version",
@@ -48,6 +51,12 @@ def load() -> ctypes.CDLL:
     lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    i, i, i, i, f, i, i, vp]
     lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
+    lib.flash_attn_bwd_preprocess.restype = i
+    lib.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_dkdv.restype = i
+    lib.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_dq.restype = i
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_status_string.argtypes = [i]
@@ -74,6 +83,24 @@ def flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes
     return load().flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace,
                                  workspace_bytes, B, H, N, d, float(scale), int(causal),
                                  int(dtype), stream)
+
+
+def flash_attn_bwd_preprocess(o, lse, dout, workspace, workspace_bytes, B, H, N, d, dtype,
+                              stream) -> int:
+    return load().flash_attn_bwd_preprocess(o, lse, dout, workspace, workspace_bytes, B, H, N, d,
+                                            int(dtype), stream)
+
+
+def flash_attn_bwd_dkdv(q, k, v, dout, workspace, workspace_bytes, dk, dv, B, H, N, d, scale,
+                        causal, dtype, stream) -> int:
+    return load().flash_attn_bwd_dkdv(q, k, v, dout, workspace, workspace_bytes, dk, dv, B, H, N,
+                                      d, float(scale), int(causal), int(dtype), stream)
+
+
+def flash_attn_bwd_dq(q, k, v, dout, workspace, workspace_bytes, dq, B, H, N, d, scale, causal,
+                      dtype, stream) -> int:
+    return load().flash_attn_bwd_dq(q, k, v, dout, workspace, workspace_bytes, dq, B, H, N, d,
+                                    float(scale), int(causal), int(dtype), stream)
 
 
 def flash_attn_bwd_workspace_bytes(B, H, N, d) -> int:

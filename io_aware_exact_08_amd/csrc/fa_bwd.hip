@@ -549,17 +549,7 @@ static hipError_t set_lds(Kern kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int D, bool BF16, bool O_F32, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
-  const int rows = p.BH * p.N;
-  {
-    constexpr int RPB = kBwdThreads / (D / 8);
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-    hipLaunchKernelGGL((bwd_pre_kernel<D, BF16, O_F32>), grid, dim3(kBwdThreads), 0, stream, p.o,
-                       (const uint16_t*)p.dout, p.lse, p.delta, p.lse2, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+static BwdArgs make_args(const BwdProblem& p) {
   BwdArgs a;
   a.q = (const uint16_t*)p.q;
   a.k = (const uint16_t*)p.k;
@@ -574,49 +564,84 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   a.BH = p.BH;
   a.c = p.scale * kLog2e;
   a.scale = p.scale;
-  {
-    a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
-    const int lds = 2 * dkdv_stage_bytes<D>();
-    auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL>;
-    hipError_t e = set_lds(kern, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
-    const int lds = 2 * dq_stage_bytes<D>();
-    auto kern = bwd_dq_kernel<D, BF16, CAUSAL>;
-    hipError_t e = set_lds(kern, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  a.n_tiles = 0;
+  return a;
 }
 
 template <int D, bool BF16, bool O_F32>
-static hipError_t launch_bwd_c(const BwdProblem& p, hipStream_t s) {
-  return p.causal ? launch_bwd_t<D, BF16, O_F32, true>(p, s) : launch_bwd_t<D, BF16, O_F32, false>(p, s);
+static hipError_t launch_pre_t(const BwdProblem& p, hipStream_t stream) {
+  const int rows = p.BH * p.N;
+  constexpr int RPB = kBwdThreads / (D / 8);
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16, O_F32>), grid, dim3(kBwdThreads), 0, stream, p.o,
+                     (const uint16_t*)p.dout, p.lse, p.delta, p.lse2, rows);
+  return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t s) {
-  switch (p.dtype) {
-    case kF16: return launch_bwd_c<D, false, false>(p, s);
-    case kBF16: return launch_bwd_c<D, true, false>(p, s);
-    case kF16OutF32: return launch_bwd_c<D, false, true>(p, s);
-    case kBF16OutF32: return launch_bwd_c<D, true, true>(p, s);
-    default: return hipErrorInvalidValue;
-  }
+template <int D, bool BF16, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdProblem& p, hipStream_t stream) {
+  BwdArgs a = make_args(p);
+  a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
+  const int lds = 2 * dkdv_stage_bytes<D>();
+  auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL>;
+  hipError_t e = set_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
+  return hipGetLastError();
 }
+
+template <int D, bool BF16, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdProblem& p, hipStream_t stream) {
+  BwdArgs a = make_args(p);
+  a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
+  const int lds = 2 * dq_stage_bytes<D>();
+  auto kern = bwd_dq_kernel<D, BF16, CAUSAL>;
+  hipError_t e = set_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Dispatch over (d, input type) and either the O type (pre) or causal.
+template <template <int, bool, bool> class L>
+static hipError_t dispatch3(const BwdProblem& p, hipStream_t s, bool third) {
+  const bool bf16 = p.dtype == kBF16 || p.dtype == kBF16OutF32;
+  if (p.dtype < kF16 || p.dtype > kBF16OutF32) return hipErrorInvalidValue;
+  if (p.d == 64) {
+    if (bf16) return third ? L<64, true, true>::run(p, s) : L<64, true, false>::run(p, s);
+    return third ? L<64, false, true>::run(p, s) : L<64, false, false>::run(p, s);
+  }
+  if (p.d == 128) {
+    if (bf16) return third ? L<128, true, true>::run(p, s) : L<128, true, false>::run(p, s);
+    return third ? L<128, false, true>::run(p, s) : L<128, false, false>::run(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+template <int D, bool BF16, bool X>
+struct PreL {
+  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_pre_t<D, BF16, X>(p, s); }
+};
+template <int D, bool BF16, bool X>
+struct DkdvL {
+  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_dkdv_t<D, BF16, X>(p, s); }
+};
+template <int D, bool BF16, bool X>
+struct DqL {
+  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_dq_t<D, BF16, X>(p, s); }
+};
+
+hipError_t launch_bwd_pre(const BwdProblem& p, hipStream_t s) {
+  return dispatch3<PreL>(p, s, p.dtype == kF16OutF32 || p.dtype == kBF16OutF32);
+}
+hipError_t launch_bwd_dkdv(const BwdProblem& p, hipStream_t s) { return dispatch3<DkdvL>(p, s, p.causal); }
+hipError_t launch_bwd_dq(const BwdProblem& p, hipStream_t s) { return dispatch3<DqL>(p, s, p.causal); }
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return launch_bwd_d<64>(p, s);
-  if (p.d == 128) return launch_bwd_d<128>(p, s);
-  return hipErrorInvalidValue;
+  hipError_t e = launch_bwd_pre(p, s);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv(p, s);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq(p, s);
 }
 
 }  // namespace fa

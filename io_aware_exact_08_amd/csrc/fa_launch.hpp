@@ -45,5 +45,8 @@ struct BwdProblem {
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdProblem& p, hipStream_t stream);
 
 }  // namespace fa

@@ -87,6 +87,78 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Shared checks of the three backward stages; fills p (pointers not listed
+// for a stage are left NULL).
+static int bwd_stage_setup(fa::BwdProblem& p, const void* workspace, size_t workspace_bytes, int B,
+                           int H, int N, int d, float scale, int causal, int dtype) {
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  p = fa::BwdProblem{};
+  p.delta = (float*)workspace;
+  p.lse2 = (float*)workspace + (size_t)B * H * N;
+  p.BH = B * H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  return FA_OK;
+}
+
+int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout, void* workspace,
+                              size_t workspace_bytes, int B, int H, int N, int d, int dtype,
+                              void* stream) {
+  if (!o || !lse || !dout) return FA_ERR_NULL;
+  fa::BwdProblem p;
+  int st = bwd_stage_setup(p, workspace, workspace_bytes, B, H, N, d, 1.0f, 0, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(o) || !aligned16(lse) || !aligned16(dout)) return FA_ERR_ALIGN;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  return fa::launch_bwd_pre(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !dout || !dk || !dv) return FA_ERR_NULL;
+  fa::BwdProblem p;
+  int st = bwd_stage_setup(p, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, dout, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.dk = dk;
+  p.dv = dv;
+  return fa::launch_bwd_dkdv(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int N,
+                      int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !dout || !dq) return FA_ERR_NULL;
+  fa::BwdProblem p;
+  int st = bwd_stage_setup(p, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, dout, dq};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.dout = dout;
+  p.dq = dq;
+  return fa::launch_bwd_dq(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
+        "flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv",
+        "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
         "flash_attn_status_string", "flash_attn_version"])
 
 
@@ -115,3 +116,32 @@ def test_product_path_has_no_oracle_or_allocation():
                 if f.endswith((".hip", ".hpp", ".cpp")):
                     for bad in ("hipMalloc", "hipFree", "hipHostMalloc", "malloc("):
                         assert bad not in text, (f, bad)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(workspace=None), 7), (dict(workspace_bytes=10), 7),
+    (dict(d=100), 3), (dict(dtype=9), 4), (dict(o=P + 4), 5), (dict(workspace=P + 4), 5),
+])
+def test_bwd_preprocess_validation(lib, kw, status):
+    args = dict(o=P, lse=P, dout=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1, N=8, d=64,
+                dtype=0, stream=None)
+    args.update(kw)
+    assert lib.flash_attn_bwd_preprocess(**args) == status
+
+
+@pytest.mark.parametrize("stage", ["dkdv", "dq"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(workspace=None), 7), (dict(N=0), 2), (dict(d=16), 3),
+    (dict(scale=0.0), 8), (dict(causal=3), 2), (dict(k=P + 2), 5),
+])
+def test_bwd_stage_validation(lib, stage, kw, status):
+    args = dict(q=P, k=P, v=P, dout=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1, N=8,
+                d=64, scale=0.125, causal=0, dtype=0, stream=None)
+    if stage == "dkdv":
+        args.update(dk=P, dv=P)
+        args.update(kw)
+        assert lib.flash_attn_bwd_dkdv(**args) == status
+    else:
+        args.update(dq=P)
+        args.update(kw)
+        assert lib.flash_attn_bwd_dq(**args) == status

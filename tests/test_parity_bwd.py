@@ -82,3 +82,34 @@ def test_bwd_deterministic_and_in_bounds():
         assert torch.equal(vw, a)
         assert (b[:pad] == 3.0).all() and (b[pad + n:] == 3.0).all()
     check_heads(w, (o, lse, *views), [(0, 0), (0, 2)])
+
+
+def test_stages_compose_to_bwd_bitwise():
+    """preprocess -> dK/dV -> dQ equals flash_attn_bwd bit for bit, also with
+    dK/dV and dQ on two streams after the preprocess."""
+    import torch
+    import io_aware_exact_08_amd as fa
+    w = si.random_case(2, 2, 333, 64, si.FMT_F16, True, seed=21, with_do=True)
+    q, k, v, do = dev_inputs(w)
+    o, lse = fa.flash_attn_fwd(q, k, v, causal=True, scale=w.scale)
+    ref = fa.flash_attn_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    ws = torch.empty(fa.workspace_bytes(2, 2, 333, 64) // 4, dtype=torch.float32, device="cuda")
+    fa.flash_attn_bwd_preprocess(o, lse, do, ws)
+    dk, dv = fa.flash_attn_bwd_dkdv(q, k, v, do, ws, causal=True, scale=w.scale)
+    dq = fa.flash_attn_bwd_dq(q, k, v, do, ws, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a_, b_ in zip((dq, dk, dv), ref):
+        assert torch.equal(a_, b_)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    fa.flash_attn_bwd_preprocess(o, lse, do, ws)
+    done = torch.cuda.Event()
+    done.record()
+    s1.wait_event(done)
+    s2.wait_event(done)
+    with torch.cuda.stream(s1):
+        dk2, dv2 = fa.flash_attn_bwd_dkdv(q, k, v, do, ws, causal=True, scale=w.scale)
+    with torch.cuda.stream(s2):
+        dq2 = fa.flash_attn_bwd_dq(q, k, v, do, ws, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for a_, b_ in zip((dq2, dk2, dv2), ref):
+        assert torch.equal(a_, b_)
