@@ -30,8 +30,10 @@ KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hip", "io_aware_exact_08_am
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The clocks take roughly 0.2 s of sustained load to settle; the default
+    # warm-up (about 0.3 s) covers that, so the timed steps see steady state.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--N", type=int, default=8192)
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--fwd-only", action="store_true",
@@ -42,6 +44,11 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the "
                          "timed loop (reference dispatch for HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 counter_collection.csv files (a "
+                         "FETCH_SIZE run and a WRITE_SIZE run of this script with "
+                         "--copy-calibration-mib) into the per-kernel HBM traffic summary")
+    ap.add_argument("--traffic-out", default=PROFILE_TRAFFIC)
     return ap.parse_args()
 
 
@@ -65,6 +72,56 @@ def traffic_from_profile(kernel):
     if rec.get("sources_sha256_16") != sources_digest():
         return None
     return rec.get("hbm_bytes_per_launch", {}).get(kernel)
+
+
+KERNEL_KEYS = ("fwd_kernel", "bwd_pre_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel")
+
+
+def _counter_rows(path, counter):
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv, out_path, calib_mib):
+    """Copy-calibrated HBM bytes per launch, per kernel of the step.
+
+    FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by
+    (bytes a plain copy of `calib_mib` MiB moves) / (what the same counter read
+    for that copy's dispatch), the copy being the largest-reading dispatch whose
+    kernel name contains "copy"."""
+    calib_kib = calib_mib * 1024.0
+    rec = {"sources_sha256_16": sources_digest(), "copy_calibration_mib": calib_mib,
+           "commands": [
+               f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 bench.py "
+               f"--no-cpu-baseline --steps 3 --warmup 1 --copy-calibration-mib {calib_mib}"
+               for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+               f"python3 bench.py --traffic-summary {fetch_csv} {write_csv}"],
+           "counter_kib_per_launch": {}, "hbm_bytes_per_launch": {}}
+    per = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, name)
+        copies = [v for kn, v in rows if "copy" in kn.lower()]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch to calibrate {name} against")
+        factor = calib_kib / max(copies)
+        rec[f"{name}_factor"] = round(factor, 4)
+        for key in KERNEL_KEYS:
+            vals = [v for kn, v in rows if f"::{key}<" in kn]
+            if vals:
+                kib = sum(vals) / len(vals)
+                rec["counter_kib_per_launch"].setdefault(key, {})[name] = round(kib, 1)
+                per.setdefault(key, 0.0)
+                per[key] += kib * 1024.0 * factor
+    rec["hbm_bytes_per_launch"] = {k_: int(round(v)) for k_, v in per.items()}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, heads):
@@ -92,6 +149,10 @@ def cpu_baseline(w, heads):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.traffic_out,
+                        args.copy_calibration_mib or 256)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
               "(the path shards by heads with no exchange; see the design notes)",

@@ -99,26 +99,29 @@ struct BwdArgs {
 };
 
 // Per-lane byte offsets shared by both kernels for a row-major LDS tile with
-// ROWB bytes per row, swizzled with swz_kq.
+// ROWB bytes per row, swizzled with swz_dual (read both as a row operand and
+// through the transposing read).
 template <int D>
 struct TileOffsets {
   static constexpr int ROWB = D * 2;
   static constexpr int DC = D / 16;
   static constexpr int DT = D / 32;
-  int rd[DC];  // row operand: rows 32t + perm_k(m), chunk 2dc+h (+ 32t*ROWB)
-  int tr[DT];  // transposing read for d tile dt, k-rows 8h + j (+ 16kc*ROWB, + 4r*ROWB)
+  int rd[DC];   // row operand: rows 32t + perm_k(m), chunk 2dc+h (+ 32t*ROWB)
+  int trl[DT];  // transposing read for d tile dt, k-rows 8h + j (+ 16kc*ROWB)
+  int trh[DT];  // the same for k-rows 8h + 4 + j
   __device__ __forceinline__ TileOffsets(int lane) {
     const int m = lane & 31, h = lane >> 5;
     const int row = perm_k(m);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) rd[dc] = row * ROWB + (((2 * dc + h) ^ swz_kq(row)) * 16);
+    for (int dc = 0; dc < DC; ++dc) rd[dc] = row * ROWB + (((2 * dc + h) ^ swz_dual<D>(row)) * 16);
     const int i = lane & 15, gg = (lane >> 4) & 1;
     const int j = i >> 2, q = i & 3;
     const int trow = 8 * h + j;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int chunk = 4 * dt + 2 * (q & 1) + gg;
-      tr[dt] = trow * ROWB + ((chunk ^ swz_kq(trow)) * 16) + (q >> 1) * 8;
+      trl[dt] = trow * ROWB + ((chunk ^ swz_dual<D>(trow)) * 16) + (q >> 1) * 8;
+      trh[dt] = (trow + 4) * ROWB + ((chunk ^ swz_dual<D>(trow + 4)) * 16) + (q >> 1) * 8;
     }
   }
 };
@@ -129,14 +132,15 @@ template <int D>
 __device__ __forceinline__ uint32_t tile_src_offset(int p) {
   constexpr int CPR = D / 8;
   const int row = p / CPR, cpos = p % CPR;
-  return (uint32_t)(row * D * 2 + ((cpos ^ swz_kq(row)) * 16));
+  return (uint32_t)(row * D * 2 + ((cpos ^ swz_dual<D>(row)) * 16));
 }
 
 // Transposed operand (A of an O^T-shaped product) for 16 k-rows starting at
 // tile row 16*kc from the transposing reads.
-__device__ __forceinline__ u32x4 tr_operand(const char* tile, int off, int kc, int rowb) {
-  const u32x2 lo = lds_read_tr16(tile + off + kc * 16 * rowb);
-  const u32x2 hi = lds_read_tr16(tile + off + kc * 16 * rowb + 4 * rowb);
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, int off_lo, int off_hi, int kc,
+                                            int rowb) {
+  const u32x2 lo = lds_read_tr16(tile + off_lo + kc * 16 * rowb);
+  const u32x2 hi = lds_read_tr16(tile + off_hi + kc * 16 * rowb);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -303,8 +307,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc) {
-        const u32x4 ga = tr_operand(sG, to.tr[dt], qc, ROWB);
-        const u32x4 qa = tr_operand(sQ, to.tr[dt], qc, ROWB);
+        const u32x4 ga = tr_operand(sG, to.trl[dt], to.trh[dt], qc, ROWB);
+        const u32x4 qa = tr_operand(sQ, to.trl[dt], to.trh[dt], qc, ROWB);
         dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
         dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
       }
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 ka = tr_operand(sK, to.tr[dt], kc, ROWB);
+        const u32x4 ka = tr_operand(sK, to.trl[dt], to.trh[dt], kc, ROWB);
         dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
       }
   };

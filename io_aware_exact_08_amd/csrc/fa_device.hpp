@@ -150,32 +150,38 @@ __device__ __forceinline__ int perm_o(int m) {
   return (((m >> 2) & 1) << 4) | ((m >> 3) << 2) | (m & 3);
 }
 
-// 16-byte-chunk XOR swizzles (in units of 8 16-bit elements) for LDS tiles.
-// Row-major [rows][cols] tile read as MFMA A operand with rows perm_k(m):
-// distinct over each group of 8 lanes.
-__device__ __forceinline__ int swz_row(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
-// Row-major V tile read through lds_read_tr16: rows 4 apart share a bank
-// window, so chunks are XORed with s(row % 4) in {0, 1, 4, 5}.
-__device__ __forceinline__ int swz_v(int r) { return (r & 1) | ((r & 2) << 1); }
-// Row-major tile read both ways: as a row operand (8 lanes on rows
-// perm_k(m), one chunk) and through lds_read_tr16 (16 lanes on rows 4 apart
-// in pairs of chunks c, c^2).  Bits 0 and 2 of the XOR follow row % 4 and
-// bit 1 follows bit 3 of the row, which keeps both patterns conflict-free.
-__device__ __forceinline__ int swz_kq(int r) { return (r & 1) | ((r & 2) << 1) | (((r >> 3) & 1) << 1); }
-// Transposed [d][keys] tile: distinct over the rows perm_o(m) of 8 lanes and
-// over rows 8*c + i (c = 0..7) written by 8 lanes.
-__device__ __forceinline__ int swz_t(int d) {
-  return ((d ^ (d >> 3)) & 1) | ((((d >> 1) ^ (d >> 5)) & 1) << 1) | (((d >> 4) & 1) << 2);
-}
+// 16-byte-chunk XOR swizzles for row-major LDS tiles of D 16-bit columns
+// (chunk c of tile row r is stored at chunk position c ^ swz(r)).
+//
+// gfx950 LDS has 64 banks of 4 bytes, i.e. a 256-byte bank window: a d=64 row
+// (128 B) shares its window with its neighbour of opposite parity, a d=128 row
+// fills one window.  ds_read_b128 serves 16 consecutive lanes per cycle and
+// ds_read_b64 (also the transposing form) 32, so a read is conflict-free when
+// those lanes land on distinct 16-byte slots of the window.
+//  - Row operand (rows perm_k(m), one chunk per instruction): the 16 lanes of
+//    a cycle cover all row residues mod 16, so the XOR must be a bijection of
+//    row bits 1..3 (d=64: bit 0 picks the window half) or of bits 0..3 (d=128).
+//  - Transposing read (lanes on rows 8h + j, j < 4, four chunks 4t..4t+3):
+//    the 32 lanes of a cycle cover row bits 0 and 1, so the XOR must move the
+//    four-chunk block by row bit 1 (d=64) or by row bits 0 and 1 (d=128).
 
-// Byte-select of two dwords: result bytes picked by `sel` (v_perm_b32).
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  // (a.lo16, b.lo16)
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+// Tiles read only as a row operand, or both ways.  The XOR depends on row bit 2,
+// so a transposing read of rows r + 4 needs its own per-lane offset.
+template <int D>
+__device__ __forceinline__ int swz_dual(int r) {
+  if constexpr (D == 64)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
+  else
+    return ((r & 1) << 2) | (((r >> 1) & 1) << 3) | ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
 }
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  // (a.hi16, b.hi16)
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+// Tiles read only through the transposing read: the XOR depends on row bits 0
+// and 1 alone, so rows r and r + 4 share one per-lane offset.
+template <int D>
+__device__ __forceinline__ int swz_tr(int r) {
+  if constexpr (D == 64)
+    return (r & 1) | (((r >> 1) & 1) << 2);
+  else
+    return ((r & 1) << 2) | (((r >> 1) & 1) << 3);
 }
 
 }  // namespace fa

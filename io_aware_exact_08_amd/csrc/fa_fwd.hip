@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   {
     const int row = perm_k(m);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) k_rd[dc] = (row * D + (((2 * dc + h) ^ swz_row(row)) * 8)) * 2;
+    for (int dc = 0; dc < DC; ++dc) k_rd[dc] = (row * D + (((2 * dc + h) ^ swz_dual<D>(row)) * 8)) * 2;
   }
   // V^T operand (A of O^T) through the transposing read.  In 16-lane group g
   // (gg = g % 2), lane i = 4j + q reads key 8h + 4r + j (r: which half of the
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int chunk = 4 * dt + 2 * (q & 1) + gg;
-      v_tr[dt] = (8 * h + j) * ROWB + ((chunk ^ swz_v(j)) * 16) + (q >> 1) * 8;
+      v_tr[dt] = (8 * h + j) * ROWB + ((chunk ^ swz_tr<D>(j)) * 16) + (q >> 1) * 8;
     }
   }
   // Direct-load slots: thread slot p = i*256 + tid holds tile row p / CPR at
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   for (int i = 0; i < LOADS; ++i) {
     const int p = i * kThreads + tid;
     const int row = p / CPR, cpos = p % CPR;
-    k_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_row(row)) * 16));
-    v_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_v(row)) * 16));
+    k_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_dual<D>(row)) * 16));
+    v_gl[i] = (uint32_t)(row * ROWB + ((cpos ^ swz_tr<D>(row)) * 16));
   }
 
   const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
