@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the "
                          "timed loop (reference dispatch for HBM byte counters)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the untimed-by-the-step per-configuration report")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 counter_collection.csv files (a "
                          "FETCH_SIZE run and a WRITE_SIZE run of this script with "
@@ -122,6 +124,58 @@ def traffic_summary(fetch_csv, write_csv, out_path, calib_mib):
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
+
+
+def config_sweep(fa, si, torch, np, dev):
+    """Event-timed forward (and backward where the configuration has one) of the
+    other synthetic configurations; reported beside the headline step, outside
+    its timed region."""
+    out = {}
+
+    def tensors(w):
+        dt = torch.float16 if w.fmt == "f16" else torch.bfloat16
+        conv = lambda b: torch.from_numpy(b.view(np.int16)).view(dt).to(dev)  # noqa: E731
+        return conv(w.q), conv(w.k), conv(w.v), (conv(w.do) if w.do is not None else None)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def run(name, w, out_f32=False, bwd=False, reps=20):
+        q, k, v, do = tensors(w)
+        B, H, N, d = w.shape
+        fl = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+        o, lse = fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out_f32=out_f32)
+        ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
+                                             out_f32=out_f32, o=o, lse=lse), reps)
+        rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal,
+               "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        if bwd:
+            ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32,
+                             device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ms_b = timed(lambda: fa.flash_attn_bwd(q, k, v, o, lse, do, causal=w.causal,
+                                                   scale=w.scale, dq=dq, dk=dk, dv=dv,
+                                                   workspace=ws), reps)
+            rec["bwd_ms"] = round(ms_b, 4)
+            rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
+        out[name] = rec
+
+    for n in (1024, 2048, 4096, 8192):
+        run(f"fwd_B2H12N{n}d64_f16", si.a100_sweep(n))
+    run("fwd_causal_B2H16N4096d128_bf16_spiked_f32out", si.spiked_causal(), out_f32=True)
+    run("fwdbwd_causal_B1H8N32768d64_bf16", si.long_causal(with_do=True), bwd=True, reps=3)
+    run("fwdbwd_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True)
+    run("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), bwd=True)
+    return out
 
 
 def cpu_baseline(w, heads):
@@ -281,6 +335,8 @@ def main():
         "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4),
         "traffic": traffic_from_profile(dom),
     }
+    if not args.no_sweep:
+        res["configs"] = config_sweep(fa, si, torch, np, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -9,6 +9,8 @@ from .attention import (  # noqa: F401
     forward_rows,
     backward,
     backward_head,
+    backward_dq_rows,
+    backward_kv_cols,
     forward_key_blocked,
     forward_query_chunked,
     forward_scalar,

@@ -143,6 +143,82 @@ def backward(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
+def backward_dq_rows(q, k, v, do, rows: Iterable, scale: float, causal: bool):
+    """dQ for selected query rows only; ``rows`` holds (b, h, i) triples.
+
+    Row i of the backward above depends on row i alone: its softmax over the
+    visible keys, O_i, D_i = dO_i . O_i, dP_ij = dO_i . v_j,
+    dS_ij = P_ij (dP_ij - D_i) and dQ_i = scale * sum_j dS_ij k_j.  Used at
+    sizes where the full matrices are too large (page 2, "Re-computation":
+    the row's probabilities are rebuilt from Q and K).
+    """
+    rows = [tuple(int(x) for x in r) for r in rows]
+    out = np.empty((len(rows), k.shape[-1]), dtype=np.float64)
+    for n, (b, h, i) in enumerate(rows):
+        kk = k[b, h, : i + 1] if causal else k[b, h]
+        vv = v[b, h, : i + 1] if causal else v[b, h]
+        s = scale * (kk @ q[b, h, i])
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        o_i = p @ vv
+        dp = vv @ do[b, h, i]
+        ds = p * (dp - do[b, h, i] @ o_i)
+        out[n] = scale * (ds @ kk)
+    return out
+
+
+def backward_kv_cols(q, k, v, do, cols: Iterable, scale: float, causal: bool,
+                     chunk: int = 1024):
+    """dK and dV for selected key rows only; ``cols`` holds (b, h, j) triples.
+
+    Key j's gradients need column j of P and dS over every query row, and
+    those need each row's LSE_i and D_i.  Per head touched, a forward over
+    query chunks of ``chunk`` rows (the same masked softmax as forward_head,
+    one chunk of the N x N matrix at a time) gives LSE and O, hence
+    D_i = dO_i . O_i; then for the selected keys
+        P_ij = exp(scale q_i . k_j - LSE_i),  dP_ij = dO_i . v_j,
+        dS_ij = P_ij (dP_ij - D_i),
+        dK_j = scale * sum_i dS_ij q_i,       dV_j = sum_i P_ij dO_i.
+    """
+    cols = [tuple(int(x) for x in c) for c in cols]
+    dk_out = np.empty((len(cols), k.shape[-1]), dtype=np.float64)
+    dv_out = np.empty((len(cols), v.shape[-1]), dtype=np.float64)
+    heads = sorted({(b, h) for b, h, _ in cols})
+    for b, h in heads:
+        qh, kh, vh, gh = q[b, h], k[b, h], v[b, h], do[b, h]
+        n = qh.shape[0]
+        lse = np.empty(n, dtype=np.float64)
+        dsum = np.empty(n, dtype=np.float64)
+        for i0 in range(0, n, chunk):
+            i1 = min(n, i0 + chunk)
+            kend = i1 if causal else kh.shape[0]
+            s = scale * (qh[i0:i1] @ kh[:kend].T)
+            if causal:
+                ii = np.arange(i0, i1)[:, None]
+                jj = np.arange(kend)[None, :]
+                s = np.where(jj <= ii, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            o = (p @ vh[:kend]) / l
+            lse[i0:i1] = (m + np.log(l))[:, 0]
+            dsum[i0:i1] = (gh[i0:i1] * o).sum(axis=1)
+        sel = [(n_, j) for n_, (bb, hh, j) in enumerate(cols) if (bb, hh) == (b, h)]
+        idx = np.array([j for _, j in sel])
+        s = scale * (qh @ kh[idx].T)                       # [N, m]
+        if causal:
+            s = np.where(idx[None, :] <= np.arange(n)[:, None], s, -np.inf)
+        p = np.exp(s - lse[:, None])
+        dp = gh @ vh[idx].T
+        ds = p * (dp - dsum[:, None])
+        dk_sel = scale * (ds.T @ qh)
+        dv_sel = p.T @ gh
+        for r, (n_, _) in enumerate(sel):
+            dk_out[n_] = dk_sel[r]
+            dv_out[n_] = dv_sel[r]
+    return dk_out, dv_out
+
+
 # ----------------------------------------------------------------------------
 # Self-check variants (pins for the definition above; never compared to GPU)
 # ----------------------------------------------------------------------------

@@ -154,12 +154,13 @@ def spiked_causal(N: int = 4096, H: int = 16) -> Workload:
                     notes={"spike": "K rows j%64==0 scaled x8"})
 
 
-def long_causal(N: int = 32768) -> Workload:
-    """Long-sequence causal fwd, B=1 H=8 d=64, bf16 N(0, 0.5^2)."""
+def long_causal(N: int = 32768, with_do: bool = False) -> Workload:
+    """Long-sequence causal attention, B=1 H=8 d=64, bf16 N(0, 0.5^2) (dO too,
+    for the backward at the same shape)."""
     shape = (1, 8, N, 64)
-    t = _draw([4, N], shape, 0.5, FMT_BF16, False)
+    t = _draw([4, N], shape, 0.5, FMT_BF16, with_do)
     return Workload(f"long_causal_B1H8N{N}d64_bf16", *shape, FMT_BF16, True, default_scale(64),
-                    t["q"], t["k"], t["v"])
+                    t["q"], t["k"], t["v"], t.get("do"))
 
 
 def long_causal_sample_rows(H: int, N: int, count: int = 256):

@@ -340,6 +340,57 @@ def test_gradient_sums():
         np.testing.assert_allclose(dv2, dv, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_gradients_equal_full_backward(causal):
+    """The per-row dQ and per-key dK/dV routines (used where the N x N matrices
+    are too large) reproduce the full backward, which the finite differences
+    above pin; the key routine's forward chunking does not change the result."""
+    B, H, N, d = 2, 2, 37, 8
+    q, k, v, do = (rand((B, H, N, d), s) for s in (70, 71, 72, 73))
+    dq, dk, dv = oracle.backward(q, k, v, do, 0.31, causal)
+    sel = [(b, h, i) for b in range(B) for h in range(H) for i in range(N)]
+    np.testing.assert_allclose(oracle.backward_dq_rows(q, k, v, do, sel, 0.31, causal),
+                               dq.reshape(-1, d), atol=1e-12)
+    for chunk in (1, 5, N, 1000):
+        dks, dvs = oracle.backward_kv_cols(q, k, v, do, sel, 0.31, causal, chunk=chunk)
+        np.testing.assert_allclose(dks, dk.reshape(-1, d), atol=1e-12)
+        np.testing.assert_allclose(dvs, dv.reshape(-1, d), atol=1e-12)
+    # a sparse, unordered selection over several heads gives the same rows
+    few = [(1, 0, 36), (0, 1, 0), (0, 1, 17), (1, 1, 5), (0, 0, 20)]
+    dks, dvs = oracle.backward_kv_cols(q, k, v, do, few, 0.31, causal, chunk=4)
+    for n, (b, h, j) in enumerate(few):
+        np.testing.assert_allclose(dks[n], dk[b, h, j], atol=1e-12)
+        np.testing.assert_allclose(dvs[n], dv[b, h, j], atol=1e-12)
+    dqs = oracle.backward_dq_rows(q, k, v, do, few, 0.31, causal)
+    for n, (b, h, i) in enumerate(few):
+        np.testing.assert_allclose(dqs[n], dq[b, h, i], atol=1e-12)
+
+
+def test_sampled_gradients_finite_difference():
+    """Direct pin of the per-row routines: central differences of <dO, O> in one
+    query row and in one key row."""
+    N, d, sc, h = 6, 3, 0.4, 1e-6
+    q, k, v, do = (rand((1, 1, N, d), s) for s in (80, 81, 82, 83))
+    for causal in (False, True):
+        def loss(q_, k_, v_):
+            o, _ = oracle.forward(q_, k_, v_, sc, causal)
+            return float((o * do).sum())
+        i, j = 4, 2
+        g_q = oracle.backward_dq_rows(q, k, v, do, [(0, 0, i)], sc, causal)[0]
+        g_k, g_v = oracle.backward_kv_cols(q, k, v, do, [(0, 0, j)], sc, causal, chunk=2)
+        for name, x, row, g in (("q", q, i, g_q), ("k", k, j, g_k[0]), ("v", v, j, g_v[0])):
+            fd = np.zeros(d)
+            for c in range(d):
+                xp, xm = x.copy(), x.copy()
+                xp[0, 0, row, c] += h
+                xm[0, 0, row, c] -= h
+                args_p, args_m = [q, k, v], [q, k, v]
+                pos = "qkv".index(name)
+                args_p[pos], args_m[pos] = xp, xm
+                fd[c] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert np.linalg.norm(fd - g) <= 1e-6 * max(np.linalg.norm(fd), 1e-12), (name, causal)
+
+
 # ----------------------------------------------------------------------------
 # Input generator and tolerance feasibility
 # ----------------------------------------------------------------------------
