@@ -149,15 +149,26 @@ def config_sweep(fa, si, torch, np, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    def run(name, w, out_f32=False, bwd=False, reps=20):
+    def run(name, w, out_f32=False, bwd=False, reps=20, splits=None):
         q, k, v, do = tensors(w)
         B, H, N, d = w.shape
         fl = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         o, lse = fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out_f32=out_f32)
-        ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
-                                             out_f32=out_f32, o=o, lse=lse), reps)
+        if splits is None:
+            ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
+                                                 out_f32=out_f32, o=o, lse=lse), reps)
+        else:
+            if splits == 0:
+                splits = fa._lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, int(w.causal))
+            ws = torch.empty(fa._lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) // 4,
+                             dtype=torch.float32, device=dev)
+            ms = timed(lambda: fa.flash_attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale,
+                                                         out_f32=out_f32, num_splits=splits,
+                                                         o=o, lse=lse, workspace=ws), reps)
         rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal,
                "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        if splits is not None:
+            rec["splits"] = splits
         if bwd:
             ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32,
                              device=dev)
@@ -173,6 +184,9 @@ def config_sweep(fa, si, torch, np, dev):
         run(f"fwd_B2H12N{n}d64_f16", si.a100_sweep(n))
     run("fwd_causal_B2H16N4096d128_bf16_spiked_f32out", si.spiked_causal(), out_f32=True)
     run("fwdbwd_causal_B1H8N32768d64_bf16", si.long_causal(with_do=True), bwd=True, reps=3)
+    few = si.random_case(1, 4, 8192, 128, "bf16", False, seed=11)
+    run("fwd_B1H4N8192d128_bf16", few, out_f32=True)
+    run("fwd_splitkv_B1H4N8192d128_bf16", few, out_f32=True, splits=0)
     run("fwdbwd_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True)
     run("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), bwd=True)
     return out

@@ -47,8 +47,9 @@ typedef enum {
   FA_ERR_DTYPE = 4,     /* unknown fa_dtype                                 */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                 */
   FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */
-  FA_ERR_WORKSPACE = 7, /* backward workspace missing or too small          */
-  FA_ERR_SCALE = 8      /* scale is not a finite positive number            */
+  FA_ERR_WORKSPACE = 7, /* workspace missing or too small                   */
+  FA_ERR_SCALE = 8,     /* scale is not a finite positive number            */
+  FA_ERR_SPLITS = 9     /* num_splits outside [1, 64]                       */
 } fa_status;
 
 /* Element types: Q/K/V (and dQ/dK/dV) type x O (and dO) type. */
@@ -129,6 +130,41 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int N, int d, float scale, int causal, int dtype,
                       void* stream);
+
+/*
+ * Split-KV forward.  The same result as flash_attn_fwd, computed as page 2's
+ * "Tiling" pass cut along the key axis: the key tiles each query tile visits
+ * are divided into num_splits contiguous ranges, each handled by its own
+ * workgroup, which keeps the chip full when B*H*N is small (few query tiles)
+ * or the keys are long.  Each range produces its own normalised O and LSE in
+ * float32 (a range with no visible key for a row gives O = 0, LSE = -inf);
+ * a second kernel merges them exactly:
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * (The online softmax's rescaling identity applied once per range instead of
+ * once per tile.)
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, causal, dtype : as flash_attn_fwd
+ *   workspace   : device buffer of >= flash_attn_fwd_splitkv_workspace_bytes
+ *                 bytes, 16-byte aligned, owned by the caller; contents on
+ *                 entry do not matter and on return are unspecified
+ *   num_splits  : 1..64 (FA_ERR_SPLITS otherwise); splits beyond the number
+ *                 of key tiles are empty and cost one idle workgroup each
+ *   Two kernels are enqueued on `stream`.
+ */
+int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, float scale, int causal, int dtype,
+                           int num_splits, void* stream);
+
+/* Bytes of workspace flash_attn_fwd_splitkv needs: 4 * num_splits * B*H*N*(d+1)
+ * (partial O and LSE); 0 for invalid arguments. */
+size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
+
+/* A split count for this shape, in 1..16: more than 1 only when the unsplit
+ * grid has at most one workgroup per compute unit and each split keeps at
+ * least 32 key tiles (splitting adds a float32 partial O per split and a merge
+ * pass, which shorter ranges do not repay). */
+int flash_attn_fwd_splitkv_default_splits(int B, int H, int N, int d, int causal);
 
 /* Bytes of workspace flash_attn_bwd needs (8 * B * H * N: two floats per row,
  * D and LSE*log2(e)); 0 for invalid sizes. */

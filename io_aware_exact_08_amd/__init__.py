@@ -4,6 +4,7 @@ The computation runs entirely in the HIP library ``libflash_attn.so``; this
 module only marshals torch tensors (device memory and streams) into its C ABI:
 
     flash_attn_fwd(q, k, v, causal=False, scale=None, out_f32=False) -> (o, lse)
+    flash_attn_fwd_splitkv(q, k, v, causal=False, scale=None, num_splits=0) -> (o, lse)
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
 
 Layout [B, H, N, d], d in {64, 128}, fp16 or bf16 inputs.
@@ -15,7 +16,7 @@ import math
 from . import _lib
 from ._lib import FlashAttnError, status_string  # noqa: F401
 
-__all__ = ["flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+__all__ = ["flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_bwd", "flash_attn_bwd_preprocess",
            "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "FlashAttnError", "status_string",
            "dtype_code", "workspace_bytes"]
 
@@ -82,6 +83,38 @@ def flash_attn_fwd(q, k, v, causal: bool = False, scale=None, out_f32: bool = Fa
                              lse.data_ptr(), B, H, N, d, sc, int(bool(causal)), code, _stream(q))
     if st != _lib.FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd")
+    return o, lse
+
+
+def flash_attn_fwd_splitkv(q, k, v, causal: bool = False, scale=None, out_f32: bool = False,
+                           num_splits: int = 0, o=None, lse=None, workspace=None):
+    """Forward with the key range split over ``num_splits`` workgroups per query
+    tile and merged (0: the library's default for this shape).  Same result
+    as flash_attn_fwd.  The float32 workspace is allocated here unless given."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    code = dtype_code(q.dtype, out_f32)
+    if num_splits == 0:
+        num_splits = _lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, int(bool(causal)))
+    odt = torch.float32 if out_f32 else q.dtype
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    _check(o, "o", (B, H, N, d), odt)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    nbytes = _lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=q.device)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), B, H, N, d,
+                                     sc, int(bool(causal)), code, num_splits, _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_splitkv")
     return o, lse
 
 

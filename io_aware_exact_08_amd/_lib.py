@@ -17,6 +17,9 @@ FA_F16, FA_BF16, FA_F16_OUT_F32, FA_BF16_OUT_F32 = 0, 1, 2, 3
 # every extern "C" symbol declared in include/flash_attn.h
 EXPORTED = (
     "flash_attn_fwd",
+    "flash_attn_fwd_splitkv",
+    "flash_attn_fwd_splitkv_workspace_bytes",
+    "flash_attn_fwd_splitkv_default_splits",
     "flash_attn_bwd",
     "flash_attn_bwd_preprocess",
     "flash_attn_bwd_dkdv",
@@ -48,6 +51,12 @@ def load() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.flash_attn_fwd.restype = i
+    lib.flash_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_fwd_splitkv.restype = i
+    lib.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.flash_attn_fwd_splitkv_workspace_bytes.restype = sz
+    lib.flash_attn_fwd_splitkv_default_splits.argtypes = [i, i, i, i, i]
+    lib.flash_attn_fwd_splitkv_default_splits.restype = i
     lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    i, i, i, i, f, i, i, vp]
     lib.flash_attn_bwd.restype = i
@@ -75,6 +84,22 @@ def flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) ->
     """Raw C call with integer device pointers; returns the fa_status."""
     return load().flash_attn_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal),
                                  int(dtype), stream)
+
+
+def flash_attn_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                           causal, dtype, num_splits, stream) -> int:
+    """Raw C call with integer device pointers; returns the fa_status."""
+    return load().flash_attn_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d,
+                                         float(scale), int(causal), int(dtype), int(num_splits),
+                                         stream)
+
+
+def flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits) -> int:
+    return int(load().flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
+
+
+def flash_attn_fwd_splitkv_default_splits(B, H, N, d, causal) -> int:
+    return int(load().flash_attn_fwd_splitkv_default_splits(B, H, N, d, int(causal)))
 
 
 def flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes,

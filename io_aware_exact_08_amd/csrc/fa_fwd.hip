@@ -104,9 +104,15 @@ struct FwdArgs {
   int BH;
   int n_qtiles;
   float c;  // scale * log2(e)
+  // split-KV: the key tiles of each query tile are cut into `splits` ranges;
+  // each workgroup writes its range's O (fp32, normalised by its own sum) and
+  // LSE to part_o [splits][BH][N][D] and part_lse [splits][BH][N].
+  int splits;
+  float* part_o;
+  float* part_lse;
 };
 
-template <int D, bool BF16, bool CAUSAL, bool OUT_F32>
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
 __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int QB = FwdCfg<D>::QB;
   constexpr int BK = FwdCfg<D>::BK;
@@ -135,17 +141,21 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   const int m = lane & 31;
   const int h = lane >> 5;
 
-  int bh, qt;
+  int bh, qt, split = 0;
   {
     const int bid = blockIdx.x;
+    const int S = SPLITKV ? a.splits : 1;
     if (CAUSAL) {
-      qt = a.n_qtiles - 1 - bid / a.BH;
-      bh = bid % a.BH;
+      qt = a.n_qtiles - 1 - bid / (a.BH * S);
+      const int rem = bid % (a.BH * S);
+      bh = rem / S;
+      split = rem % S;
     } else {
       const int G = gridDim.x;
       const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-      bh = lin / a.n_qtiles;
-      qt = lin % a.n_qtiles;
+      bh = lin / (a.n_qtiles * S);
+      qt = (lin / S) % a.n_qtiles;
+      split = lin % S;
     }
   }
   const int N = a.N;
@@ -220,10 +230,16 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   }
 
   const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
-  const int n_kt = (kend + BK - 1) / BK;
+  // This workgroup's key tiles: j0 .. j0 + n_kt - 1 (all of them unless split).
+  int j0 = 0, n_kt = (kend + BK - 1) / BK;
+  if constexpr (SPLITKV) {
+    const int total = n_kt;
+    j0 = (int)(((long long)split * total) / a.splits);
+    n_kt = (int)(((long long)(split + 1) * total) / a.splits) - j0;
+  }
 
   auto issue_tile = [&](int j, uint16_t* dk, uint16_t* dv) {
-    const uint32_t soff = (uint32_t)(j * BK * ROWB);
+    const uint32_t soff = (uint32_t)((j0 + j) * BK * ROWB);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       char* kb = (char*)dk + (i * kThreads + wave * 64) * 16;
@@ -380,6 +396,9 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
             m_new = first ? mx : fmaxf(m_run[qb], mx);
           }
           if (!need[qb]) m_new = m_run[qb];
+          // a row with no visible key so far (possible in a split of the key
+          // range) keeps a finite reference: its probabilities are all 0
+          if (m_new == -INFINITY) m_new = 0.f;
           if (!first) {
             const float alpha = fast_exp2(m_run[qb] - m_new);
             l_run[qb] *= alpha;
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
         }
-        const float neg_m = -m_run[qb];
+        const float neg_m = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
         float ls32[2] = {0.f, 0.f};
 #pragma unroll
@@ -558,7 +577,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     // never used; keeping it unconditional keeps it in one basic block with
     // the exponentials.
     auto issue_next = [&]() { nxt = compute_scores(sK[(st + 1) % kStages]); };
-    const int k0 = j * BK;
+    const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
     if (active) {
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
@@ -597,6 +616,34 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+  // A row that saw no key (only possible in a split) has l = 0: O = 0 and
+  // LSE = -inf, which the split merge weights by zero.
+  if constexpr (SPLITKV) {
+    const size_t pbase = ((size_t)split * a.BH + bh) * (size_t)N;
+    const brsrc_t ro = make_rsrc(a.part_o + pbase * D, (uint32_t)N * D * 4);
+    const brsrc_t rl = make_rsrc(a.part_lse + pbase, (uint32_t)N * 4);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = qw0 + qb * 32 + m;
+      const float lt = sum_halves(l_run[qb]);
+      const float ll = BF16 ? sum_halves(l32_run[qb]) : lt;
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int col = dt * 32 + 16 * h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[t] = __float_as_uint(oacc[qb][dt][4 * e + t] * inv);
+          bstore16(w, ro, (uint32_t)((row * D + col + 4 * e) * 4), 0);
+        }
+      }
+      if (h == 0)
+        bstore4(ll > 0.f ? (m_run[qb] + fast_log2(ll)) * kLn2 : -INFINITY, rl, (uint32_t)(row * 4), 0);
+    }
+    return;
+  }
   const brsrc_t ro = make_rsrc((const char*)a.o + base * (OUT_F32 ? 4 : 2),
                                (uint32_t)N * D * (OUT_F32 ? 4 : 2));
   const brsrc_t rl = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
@@ -632,7 +679,41 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool OUT_F32>
+// Split-KV merge (one pass over the partial results): per row,
+// LSE = logsumexp_s LSE_s and O = sum_s exp(LSE_s - LSE) O_s.  Splits whose
+// range held no visible key carry LSE_s = -inf and weigh nothing.
+template <int D, bool BF16, bool OUT_F32>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* part_o, const float* part_lse,
+                                                       void* o, float* lse, int rows, int splits) {
+  constexpr int L = D / 4;        // lanes per row, four values each
+  constexpr int RPB = 256 / L;    // rows per workgroup
+  const int row = blockIdx.x * RPB + (int)threadIdx.x / L;
+  const int col = ((int)threadIdx.x % L) * 4;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[(size_t)s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float w = fast_exp2((part_lse[(size_t)s * rows + row] - mx) * kLog2e);
+      const f32x4 x = *(const f32x4*)(part_o + ((size_t)s * rows + row) * D + col);
+      wsum += w;
+      acc += w * x;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  acc *= inv;
+  if constexpr (OUT_F32) {
+    *(f32x4*)((float*)o + (size_t)row * D + col) = acc;
+  } else {
+    u32x2 w2 = {pack2<BF16>(acc[0], acc[1]), pack2<BF16>(acc[2], acc[3])};
+    *(u32x2*)((uint16_t*)o + (size_t)row * D + col) = w2;
+  }
+  if (col == 0) lse[row] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY;
+}
+
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
 static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   constexpr int BQ = kWaves * FwdCfg<D>::QB * 32;
   FwdArgs a;
@@ -645,31 +726,51 @@ static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   a.BH = p.BH;
   a.n_qtiles = (p.N + BQ - 1) / BQ;
   a.c = p.scale * kLog2e;
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles));
-  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, OUT_F32>), grid, dim3(kThreads), 0, stream, a);
+  a.splits = SPLITKV ? p.splits : 1;
+  a.part_o = SPLITKV ? p.part : nullptr;
+  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * p.BH * p.N * D : nullptr;
+  const dim3 grid((unsigned)(a.BH * a.n_qtiles * a.splits));
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, OUT_F32, SPLITKV>), grid, dim3(kThreads), 0, stream, a);
+  if (!SPLITKV) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = p.BH * p.N;
+  constexpr int RPB = 256 / (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<D, BF16, OUT_F32>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                     dim3(256), 0, stream, a.part_o, a.part_lse, p.o, p.lse, rows, p.splits);
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool OUT_F32>
+template <int D, bool BF16, bool OUT_F32, bool SPLITKV>
 static hipError_t launch_fwd_c(const FwdProblem& p, hipStream_t s) {
-  return p.causal ? launch_fwd_t<D, BF16, true, OUT_F32>(p, s) : launch_fwd_t<D, BF16, false, OUT_F32>(p, s);
+  return p.causal ? launch_fwd_t<D, BF16, true, OUT_F32, SPLITKV>(p, s)
+                  : launch_fwd_t<D, BF16, false, OUT_F32, SPLITKV>(p, s);
 }
 
-template <int D>
+template <int D, bool SPLITKV>
 static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
   switch (p.dtype) {
-    case kF16: return launch_fwd_c<D, false, false>(p, s);
-    case kBF16: return launch_fwd_c<D, true, false>(p, s);
-    case kF16OutF32: return launch_fwd_c<D, false, true>(p, s);
-    case kBF16OutF32: return launch_fwd_c<D, true, true>(p, s);
+    case kF16: return launch_fwd_c<D, false, false, SPLITKV>(p, s);
+    case kBF16: return launch_fwd_c<D, true, false, SPLITKV>(p, s);
+    case kF16OutF32: return launch_fwd_c<D, false, true, SPLITKV>(p, s);
+    case kBF16OutF32: return launch_fwd_c<D, true, true, SPLITKV>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return launch_fwd_d<64>(p, s);
-  if (p.d == 128) return launch_fwd_d<128>(p, s);
+  if (p.d == 64) return launch_fwd_d<64, false>(p, s);
+  if (p.d == 128) return launch_fwd_d<128, false>(p, s);
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_fwd_splitkv(const FwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return launch_fwd_d<64, true>(p, s);
+  if (p.d == 128) return launch_fwd_d<128, true>(p, s);
+  return hipErrorInvalidValue;
+}
+
+int fwd_key_tile(int d) { return d == 64 ? FwdCfg<64>::BK : FwdCfg<128>::BK; }
+int fwd_query_tile(int d) { return kWaves * (d == 64 ? FwdCfg<64>::QB : FwdCfg<128>::QB) * 32; }
 
 }  // namespace fa

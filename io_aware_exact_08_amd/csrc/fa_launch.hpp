@@ -21,6 +21,8 @@ struct FwdProblem {
   float scale;
   bool causal;
   int dtype;
+  int splits = 1;         // split-KV only: key-range splits
+  float* part = nullptr;  // split-KV only: partial O then partial LSE (fp32)
 };
 
 struct BwdProblem {
@@ -44,6 +46,9 @@ struct BwdProblem {
 };
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_splitkv(const FwdProblem& p, hipStream_t stream);
+int fwd_key_tile(int d);    // keys per forward tile
+int fwd_query_tile(int d);  // query rows per forward workgroup
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdProblem& p, hipStream_t stream);

@@ -27,8 +27,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv",
-        "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
+        "flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_bytes",
+        "flash_attn_fwd_splitkv_default_splits", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+        "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
         "flash_attn_status_string", "flash_attn_version"])
 
 
@@ -40,9 +41,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.flash_attn_version() >= 100
+    assert lib.flash_attn_version() >= 101
     assert lib.status_string(0) == "ok"
-    for st in range(1, 9):
+    for st in range(1, 10):
         assert lib.status_string(st) not in ("ok", "unknown status")
     assert lib.status_string(99) == "unknown status"
 
@@ -145,3 +146,35 @@ def test_bwd_stage_validation(lib, stage, kw, status):
         args.update(dq=P)
         args.update(kw)
         assert lib.flash_attn_bwd_dq(**args) == status
+
+
+def test_splitkv_workspace_and_default_splits(lib):
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(2, 12, 1024, 64, 3) == 4 * 3 * 24 * 1024 * 65
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 8, 128, 1) == 4 * 8 * 129
+    for bad in (dict(num_splits=0), dict(num_splits=65), dict(d=96), dict(N=0)):
+        args = dict(B=1, H=1, N=8, d=64, num_splits=2)
+        args.update(bad)
+        assert lib.flash_attn_fwd_splitkv_workspace_bytes(**args) == 0
+    # splits only when the unsplit grid has <= 256 workgroups, aiming at 512,
+    # with >= 32 key tiles per split
+    assert lib.flash_attn_fwd_splitkv_default_splits(2, 12, 8192, 64, 0) == 1
+    assert lib.flash_attn_fwd_splitkv_default_splits(2, 12, 1024, 64, 0) == 1
+    assert lib.flash_attn_fwd_splitkv_default_splits(1, 4, 8192, 128, 0) == 2
+    assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 8192, 64, 0) == 4
+    assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 16384, 64, 1) == 4
+    assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 64, 64, 0) == 1
+    for B, H, N, d, c in ((1, 1, 1, 64, 0), (4, 4, 300, 128, 1), (1, 8, 32768, 64, 1)):
+        assert 1 <= lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, c) <= 16
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=5), 4),
+    (dict(num_splits=0), 9), (dict(num_splits=65), 9), (dict(workspace=None), 7),
+    (dict(workspace_bytes=4 * 2 * 8 * 65 - 1), 7), (dict(workspace=P + 4), 5), (dict(o=P + 8), 5),
+    (dict(scale=-2.0), 8), (dict(causal=5), 2),
+])
+def test_fwd_splitkv_validation(lib, kw, status):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1, N=8,
+                d=64, scale=0.125, causal=0, dtype=0, num_splits=2, stream=None)
+    args.update(kw)
+    assert lib.flash_attn_fwd_splitkv(**args) == status

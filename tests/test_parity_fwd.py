@@ -189,3 +189,60 @@ def test_errors_through_binding():
     with pytest.raises(fa.FlashAttnError) as ei:
         fa.flash_attn_fwd(y, y, y)
     assert ei.value.status == 3
+
+
+# ----------------------------------------------------------------------------
+# split-KV forward (key range cut over several workgroups, merged by LSE)
+# ----------------------------------------------------------------------------
+def run_splitkv(w, num_splits, out_f32=False):
+    import torch
+    import io_aware_exact_08_amd as fa
+    q, k, v = dev_inputs(w)[:3]
+    o, lse = fa.flash_attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, out_f32=out_f32,
+                                       num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, True)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,splits", [(1, 1), (1, 3), (37, 2), (64, 5), (200, 2), (200, 3),
+                                      (520, 4), (520, 64), (1000, 7)])
+def test_splitkv_small_shapes(N, splits, d, causal, fmt, out_f32):
+    """Every split count from one to more splits than key tiles (empty ranges),
+    ragged N, both head dims, causal ranges that end before some rows begin."""
+    w = si.random_case(1, 2, N, d, fmt, causal, seed=3 * N + d + splits)
+    o, lse = run_splitkv(w, splits, out_f32=out_f32)
+    check(w, o, lse, tag=f" splits={splits}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_a100_shape(causal):
+    """B=2 H=12 N=1024 d=64 fp16 (the A100 table's smallest N) in three splits,
+    every element; also within the bound of the unsplit forward's output."""
+    w = si.a100_sweep(1024)
+    w.causal = causal
+    o, lse = run_splitkv(w, 3)
+    check(w, o, lse, tag=" splits=3")
+    o1, l1 = run_fwd(w)
+    assert (o.float() - o1.float()).abs().max().item() <= 2e-3
+    assert (lse - l1).abs().max().item() <= 1e-3
+
+
+def test_splitkv_default_splits_few_heads():
+    """B=1 H=4 N=8192 d=128 bf16 (fp32 O), where the default splits the key
+    range (256 unsplit workgroups), on sampled rows."""
+    import io_aware_exact_08_amd as fa
+    w = si.random_case(1, 4, 8192, 128, si.FMT_BF16, False, seed=11)
+    assert fa._lib.flash_attn_fwd_splitkv_default_splits(1, 4, 8192, 128, 0) == 2
+    o, lse = run_splitkv(w, 0, out_f32=True)
+    check(w, o, lse, rows=sample_rows(w, 256, 11), tag=" default splits")
+
+
+def test_splitkv_long_causal_sampled():
+    """B=1 H=8 N=32768 d=64 bf16 causal, 16 splits, on the sampled rows."""
+    w = si.long_causal()
+    o, lse = run_splitkv(w, 16)
+    rows = [(0, int(h), int(i)) for h, i in si.long_causal_sample_rows(w.H, w.N)]
+    check(w, o, lse, rows=rows, tag=" splits=16")
