@@ -132,6 +132,31 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       void* stream);
 
 /*
+ * Forward with an additive attention bias.  Page 2, "工程落地的关键考量",
+ * suggests an attention bias to mask scores at very long sequences; this
+ * adds one to every score before the softmax:
+ *     O = softmax(scale * Q K^T + bias) V,
+ *     LSE_i = ln sum_{j visible} exp(scale * q_i . k_j + bias_ij)
+ * (-inf entries hide keys; the causal flag still applies on top).  A row
+ * whose every score is -inf gets O = 0 and LSE = -inf.
+ *
+ *   bias          : input type (fp16 / bf16, as dtype), read-only.  For batch
+ *                   b and head h the bias is the row-major N x N block at
+ *                   element offset b*bias_stride_b + h*bias_stride_h (rows of N
+ *                   elements, row i = query i, column j = key j); a stride of 0
+ *                   broadcasts over that axis.  Entries are finite or -inf.
+ *   bias_stride_b, bias_stride_h : element strides, >= 0 (FA_ERR_SHAPE),
+ *                   multiples of 8 (FA_ERR_ALIGN)
+ *   other arguments as flash_attn_fwd; in addition N must be a multiple of 8
+ *   (16-byte bias rows; FA_ERR_ALIGN) and at most 46340 (one head's bias spans
+ *   < 2^32 bytes; FA_ERR_SHAPE).
+ */
+int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                        long long bias_stride_b, long long bias_stride_h, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal, int dtype,
+                        void* stream);
+
+/*
  * Split-KV forward.  The same result as flash_attn_fwd, computed as page 2's
  * "Tiling" pass cut along the key axis: the key tiles each query tile visits
  * are divided into num_splits contiguous ranges, each handled by its own

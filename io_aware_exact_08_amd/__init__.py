@@ -4,6 +4,7 @@ The computation runs entirely in the HIP library ``libflash_attn.so``; this
 module only marshals torch tensors (device memory and streams) into its C ABI:
 
     flash_attn_fwd(q, k, v, causal=False, scale=None, out_f32=False) -> (o, lse)
+    flash_attn_fwd_bias(q, k, v, bias, causal=False, scale=None) -> (o, lse)
     flash_attn_fwd_splitkv(q, k, v, causal=False, scale=None, num_splits=0) -> (o, lse)
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
 
@@ -16,7 +17,7 @@ import math
 from . import _lib
 from ._lib import FlashAttnError, status_string  # noqa: F401
 
-__all__ = ["flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+__all__ = ["flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv", "flash_attn_bwd", "flash_attn_bwd_preprocess",
            "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "FlashAttnError", "status_string",
            "dtype_code", "workspace_bytes"]
 
@@ -83,6 +84,39 @@ def flash_attn_fwd(q, k, v, causal: bool = False, scale=None, out_f32: bool = Fa
                              lse.data_ptr(), B, H, N, d, sc, int(bool(causal)), code, _stream(q))
     if st != _lib.FA_OK:
         raise FlashAttnError(st, "flash_attn_fwd")
+    return o, lse
+
+
+def flash_attn_fwd_bias(q, k, v, bias, causal: bool = False, scale=None, out_f32: bool = False,
+                        o=None, lse=None):
+    """Forward with an additive attention bias: softmax(scale Q K^T + bias) V.
+
+    ``bias`` has the input dtype and shape [N, N], [H, N, N], [B, H, N, N] or
+    any shape that broadcasts to [B, H, N, N] with contiguous [N, N] rows
+    (e.g. an expanded view); -inf entries hide keys."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    if not bias.is_cuda or bias.dtype != q.dtype:
+        raise TypeError("bias must be a device tensor of the input dtype")
+    bb = bias.expand(B, H, N, N)
+    if bb.stride(3) != 1 or bb.stride(2) != N:
+        raise ValueError("bias rows must be contiguous [N, N] blocks")
+    code = dtype_code(q.dtype, out_f32)
+    odt = torch.float32 if out_f32 else q.dtype
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    _check(o, "o", (B, H, N, d), odt)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_fwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bb.data_ptr(),
+                                  bb.stride(0), bb.stride(1), o.data_ptr(), lse.data_ptr(),
+                                  B, H, N, d, sc, int(bool(causal)), code, _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_bias")
     return o, lse
 
 

@@ -17,6 +17,7 @@ FA_F16, FA_BF16, FA_F16_OUT_F32, FA_BF16_OUT_F32 = 0, 1, 2, 3
 # every extern "C" symbol declared in include/flash_attn.h
 EXPORTED = (
     "flash_attn_fwd",
+    "flash_attn_fwd_bias",
     "flash_attn_fwd_splitkv",
     "flash_attn_fwd_splitkv_workspace_bytes",
     "flash_attn_fwd_splitkv_default_splits",
@@ -51,6 +52,9 @@ def load() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.flash_attn_fwd.restype = i
+    ll = ctypes.c_longlong
+    lib.flash_attn_fwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_fwd_bias.restype = i
     lib.flash_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, i, vp]
     lib.flash_attn_fwd_splitkv.restype = i
     lib.flash_attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -84,6 +88,13 @@ def flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) ->
     """Raw C call with integer device pointers; returns the fa_status."""
     return load().flash_attn_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal),
                                  int(dtype), stream)
+
+
+def flash_attn_fwd_bias(q, k, v, bias, bias_stride_b, bias_stride_h, o, lse, B, H, N, d, scale,
+                        causal, dtype, stream) -> int:
+    """Raw C call with integer device pointers; returns the fa_status."""
+    return load().flash_attn_fwd_bias(q, k, v, bias, int(bias_stride_b), int(bias_stride_h), o, lse,
+                                      B, H, N, d, float(scale), int(causal), int(dtype), stream)
 
 
 def flash_attn_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,

@@ -110,9 +110,14 @@ struct FwdArgs {
   int splits;
   float* part_o;
   float* part_lse;
+  // additive attention bias (input type, [N][N] rows per (b, h) at element
+  // offset b*bias_sb + h*bias_sh; 0 strides broadcast)
+  const uint16_t* bias;
+  long long bias_sb, bias_sh;
+  int H;
 };
 
-template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV, bool BIAS>
 __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int QB = FwdCfg<D>::QB;
   constexpr int BK = FwdCfg<D>::BK;
@@ -124,12 +129,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   constexpr int CPR = D / 8;   // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;  // bytes per K/V row
   constexpr int LOADS = BK * CPR / kThreads;  // 16-byte slots per thread per tile
-  // fp16 at d=64 folds the softmax scale into a split Q (see below); bf16 and
-  // d=128 multiply the scores by the scale on the VALU.
-#ifndef FA_FWD_SPLIT
-#define FA_FWD_SPLIT 0
-#endif
-  constexpr bool SPLIT = FA_FWD_SPLIT && !BF16 && D == 64;
   static_assert(LOADS * kThreads == BK * CPR, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][BK * D];
@@ -165,6 +164,10 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
   const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
   const int qw0 = qt * BQ + wave * (QB * 32);  // first query row of this wave
+  // Attention bias rows of this head (N*N*2 < 2^32 is checked by the API).
+  const brsrc_t rb =
+      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
+                BIAS ? (uint32_t)N * N * 2 : 0u);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query m, half h), slot i
   // holds d = 16*dc + 8*h + i.  Rows past N read as 0.
@@ -174,28 +177,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       qf[qb][dc] = bload16(rq, (uint32_t)(((qw0 + qb * 32 + m) * D + dc * 16 + 8 * h) * 2), 0);
-
-  // fp16, d=64: fold c = scale*log2(e) into Q as an unevaluated pair c*Q = hi + lo
-  // of fp16 values (about 22 significant bits), so that K Qhi^T + K Qlo^T is
-  // c*s with fp32 accumulation and no per-score multiply.
-  u32x4 qlo[QB][DC];
-  if constexpr (SPLIT) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = qf[qb][dc][e];
-          const float y0 = to_f32<false>((uint16_t)(w & 0xffffu)) * a.c;
-          const float y1 = to_f32<false>((uint16_t)(w >> 16)) * a.c;
-          const uint32_t hi = pack2<false>(y0, y1);
-          const float r0 = y0 - to_f32<false>((uint16_t)(hi & 0xffffu));
-          const float r1 = y1 - to_f32<false>((uint16_t)(hi >> 16));
-          qf[qb][dc][e] = hi;
-          qlo[qb][dc][e] = pack2<false>(r0, r1);
-        }
-  }
 
   // K operand (A of S^T): row kt*32 + perm_k(m), chunk 2dc+h, swizzled.
   int k_rd[DC];
@@ -255,9 +236,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   f32x16 oacc[QB][DT];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    // Split-path scores carry the reference subtracted inside the MFMA, so it
-    // starts finite; the first tile always re-derives it from the row max.
-    m_run[qb] = SPLIT ? 0.f : -INFINITY;
+    m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
     l32_run[qb] = 0.f;
 #pragma unroll
@@ -267,25 +246,30 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   const float c = a.c;
 
   // S^T = K Q^T for one K tile (the scores of 32*KT keys against this wave's
-  // query blocks).
-  // Split path: v = c*s - bias with bias = m_run when the MFMAs were issued
-  // (the accumulators start at -bias); otherwise v = s.
+  // query blocks), and with an attention bias its raw bias values: register
+  // group g = r/8 of key block kt holds keys k_first + 32kt + 16g + 8h + 0..7,
+  // eight consecutive entries of this lane's bias row (one 16-byte load).
   struct Scores {
     f32x16 v[QB][KT];
-    float bias[QB];
+    u32x4 ab[QB][KT][2];
   };
-  auto compute_scores = [&](const uint16_t* Ks) {
+  auto compute_scores = [&](const uint16_t* Ks, int k_first) {
     const char* Kb = (const char*)Ks;
     Scores sc;
+    if constexpr (BIAS) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      sc.bias[qb] = m_run[qb];
-      f32x16 init;
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) init[r] = SPLIT ? -m_run[qb] : 0.f;
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) sc.v[qb][kt] = init;
+          for (int g = 0; g < 2; ++g)
+            sc.ab[qb][kt][g] = bload16(
+                rb, (uint32_t)(((qw0 + qb * 32 + m) * N + k_first + 32 * kt + 16 * g + 8 * h) * 2), 0);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) sc.v[qb][kt] = f32x16{};
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -294,7 +278,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
-          if constexpr (SPLIT) sc.v[qb][kt] = mfma32<BF16>(af, qlo[qb][dc], sc.v[qb][kt]);
         }
       }
     return sc;
@@ -311,6 +294,26 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* Vb = (const char*)Vs;
     auto& s = sc.v;
+    if constexpr (BIAS) {
+      // s + bias / scale, so that c * (s + bias/scale) = c*s + bias*log2(e);
+      // applied before the mask, which then overrides whatever the bias read
+      // past the end of a row.
+      const float kb = kLog2e / c;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t w = sc.ab[qb][kt][g][e];
+              s[qb][kt][8 * g + 2 * e] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w & 0xffffu)), kb,
+                                                        s[qb][kt][8 * g + 2 * e]);
+              s[qb][kt][8 * g + 2 * e + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w >> 16)), kb,
+                                                            s[qb][kt][8 * g + 2 * e + 1]);
+            }
+    }
     // O^T += V^T P^T for packed probabilities pf.
     auto pv = [&](const u32x4 (&pf)[QB][KC]) {
 #pragma unroll
@@ -353,14 +356,8 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 8 * half + 2 * e;
-              float x0, x1;
-              if constexpr (SPLIT) {
-                x0 = s[qb][kt][r];
-                x1 = s[qb][kt][r + 1];
-              } else {
-                x0 = __builtin_fmaf(s[qb][kt][r], c, neg_m);
-                x1 = __builtin_fmaf(s[qb][kt][r + 1], c, neg_m);
-              }
+              const float x0 = __builtin_fmaf(s[qb][kt][r], c, neg_m);
+              const float x1 = __builtin_fmaf(s[qb][kt][r + 1], c, neg_m);
               w[e] = pack2<false>(fast_exp2(x0), fast_exp2(x1));
               if (e & 1) t1 = sum2<false>(w[e], t1); else t0 = sum2<false>(w[e], t0);
             }
@@ -386,15 +383,8 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
               mx0 = fmaxf(mx0, fmaxf(s[qb][kt][r], s[qb][kt][r + 1]));
               mx1 = fmaxf(mx1, fmaxf(s[qb][kt][r + 2], s[qb][kt][r + 3]));
             }
-          float m_new;
-          if constexpr (SPLIT) {
-            const float delta = sc.bias[qb] - m_run[qb];  // v + delta = c*s - m_run
-            const float mx = max_halves(fmaxf(mx0, mx1)) + delta;
-            m_new = first ? m_run[qb] + mx : (mx > 0.f ? m_run[qb] + mx : m_run[qb]);
-          } else {
-            const float mx = max_halves(fmaxf(mx0, mx1)) * c;
-            m_new = first ? mx : fmaxf(m_run[qb], mx);
-          }
+          const float mx = max_halves(fmaxf(mx0, mx1)) * c;
+          float m_new = first ? mx : fmaxf(m_run[qb], mx);
           if (!need[qb]) m_new = m_run[qb];
           // a row with no visible key so far (possible in a split of the key
           // range) keeps a finite reference: its probabilities are all 0
@@ -405,11 +395,6 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
           }
-          if constexpr (SPLIT) {
-            const float shift = sc.bias[qb] - m_new;  // v + shift = c*s - m_new
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) s[qb][kt] += shift;
-          }
           m_run[qb] = m_new;
           float ts;
           exp_pack(qb, pf[qb], ts);
@@ -417,12 +402,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
         }
         pv(pf);
       };
-      bool stale = first;
-      if constexpr (SPLIT) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) stale = stale || (__ballot(sc.bias[qb] != m_run[qb]) != 0ull);
-      }
-      if (stale) {
+      if (first) {
         issue_next();
         bool need[QB];
 #pragma unroll
@@ -451,7 +431,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
         // operand reads first, then one MFMA per group of VALU instructions.
         __builtin_amdgcn_sched_group_barrier(0x100, DC * KT, 0);
 #pragma unroll
-        for (int i = 0; i < QB * KT * DC * (SPLIT ? 2 : 1); ++i) {
+        for (int i = 0; i < QB * KT * DC; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_SCHED_VALU, 0);
         }
@@ -576,7 +556,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     // On the last tile this reads a stale (in-bounds) stage whose scores are
     // never used; keeping it unconditional keeps it in one basic block with
     // the exponentials.
-    auto issue_next = [&]() { nxt = compute_scores(sK[(st + 1) % kStages]); };
+    auto issue_next = [&]() { nxt = compute_scores(sK[(st + 1) % kStages], (j0 + j + 1) * BK); };
     const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
     if (active) {
@@ -606,7 +586,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     wait_vmem();
   }
   __syncthreads();
-  Scores sa = compute_scores(sK[0]);
+  Scores sa = compute_scores(sK[0], j0 * BK);
   Scores sb;
   for (int j = 0; j < n_kt; j += 4) {
     iteration(j, std::integral_constant<int, 0>{}, sa, sb);
@@ -652,7 +632,8 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     const int row = qw0 + qb * 32 + m;  // rows past N are dropped by the stores
     const float lt = sum_halves(l_run[qb]);
     const float ll = BF16 ? sum_halves(l32_run[qb]) : lt;
-    const float inv = 1.0f / lt;
+    // a bias can hide every key of a row: then O = 0 and LSE = -inf
+    const float inv = (!BIAS || lt > 0.f) ? 1.0f / lt : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int col = dt * 32 + 16 * h;
@@ -675,7 +656,9 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
         }
       }
     }
-    if (h == 0) bstore4((m_run[qb] + fast_log2(ll)) * kLn2, rl, (uint32_t)(row * 4), 0);
+    if (h == 0)
+      bstore4((!BIAS || ll > 0.f) ? (m_run[qb] + fast_log2(ll)) * kLn2 : -INFINITY, rl,
+              (uint32_t)(row * 4), 0);
   }
 }
 
@@ -713,7 +696,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* part_o, con
   if (col == 0) lse[row] = wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV, bool BIAS>
 static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   constexpr int BQ = kWaves * FwdCfg<D>::QB * 32;
   FwdArgs a;
@@ -729,8 +712,13 @@ static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   a.splits = SPLITKV ? p.splits : 1;
   a.part_o = SPLITKV ? p.part : nullptr;
   a.part_lse = SPLITKV ? p.part + (size_t)p.splits * p.BH * p.N * D : nullptr;
+  a.bias = (const uint16_t*)p.bias;
+  a.bias_sb = p.bias_sb;
+  a.bias_sh = p.bias_sh;
+  a.H = p.H;
   const dim3 grid((unsigned)(a.BH * a.n_qtiles * a.splits));
-  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, OUT_F32, SPLITKV>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, OUT_F32, SPLITKV, BIAS>), grid, dim3(kThreads), 0,
+                     stream, a);
   if (!SPLITKV) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -741,32 +729,34 @@ static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool OUT_F32, bool SPLITKV>
+template <int D, bool BF16, bool OUT_F32, bool SPLITKV, bool BIAS>
 static hipError_t launch_fwd_c(const FwdProblem& p, hipStream_t s) {
-  return p.causal ? launch_fwd_t<D, BF16, true, OUT_F32, SPLITKV>(p, s)
-                  : launch_fwd_t<D, BF16, false, OUT_F32, SPLITKV>(p, s);
+  return p.causal ? launch_fwd_t<D, BF16, true, OUT_F32, SPLITKV, BIAS>(p, s)
+                  : launch_fwd_t<D, BF16, false, OUT_F32, SPLITKV, BIAS>(p, s);
 }
 
-template <int D, bool SPLITKV>
+template <int D, bool SPLITKV, bool BIAS>
 static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
   switch (p.dtype) {
-    case kF16: return launch_fwd_c<D, false, false, SPLITKV>(p, s);
-    case kBF16: return launch_fwd_c<D, true, false, SPLITKV>(p, s);
-    case kF16OutF32: return launch_fwd_c<D, false, true, SPLITKV>(p, s);
-    case kBF16OutF32: return launch_fwd_c<D, true, true, SPLITKV>(p, s);
+    case kF16: return launch_fwd_c<D, false, false, SPLITKV, BIAS>(p, s);
+    case kBF16: return launch_fwd_c<D, true, false, SPLITKV, BIAS>(p, s);
+    case kF16OutF32: return launch_fwd_c<D, false, true, SPLITKV, BIAS>(p, s);
+    case kBF16OutF32: return launch_fwd_c<D, true, true, SPLITKV, BIAS>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return launch_fwd_d<64, false>(p, s);
-  if (p.d == 128) return launch_fwd_d<128, false>(p, s);
+  const bool bias = p.bias != nullptr;
+  if (p.d == 64) return bias ? launch_fwd_d<64, false, true>(p, s) : launch_fwd_d<64, false, false>(p, s);
+  if (p.d == 128) return bias ? launch_fwd_d<128, false, true>(p, s) : launch_fwd_d<128, false, false>(p, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_splitkv(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return launch_fwd_d<64, true>(p, s);
-  if (p.d == 128) return launch_fwd_d<128, true>(p, s);
+  if (p.bias != nullptr) return hipErrorInvalidValue;
+  if (p.d == 64) return launch_fwd_d<64, true, false>(p, s);
+  if (p.d == 128) return launch_fwd_d<128, true, false>(p, s);
   return hipErrorInvalidValue;
 }
 

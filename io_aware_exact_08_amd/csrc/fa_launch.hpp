@@ -23,6 +23,9 @@ struct FwdProblem {
   int dtype;
   int splits = 1;         // split-KV only: key-range splits
   float* part = nullptr;  // split-KV only: partial O then partial LSE (fp32)
+  int H = 1;              // heads per batch entry (bias addressing)
+  const void* bias = nullptr;  // additive attention bias, or null
+  long long bias_sb = 0, bias_sh = 0;
 };
 
 struct BwdProblem {

@@ -48,6 +48,38 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return fa::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                        long long bias_stride_b, long long bias_stride_h, void* o, float* lse,
+                        int B, int H, int N, int d, float scale, int causal, int dtype,
+                        void* stream) {
+  if (!q || !k || !v || !bias || !o || !lse) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (N > 46340) return FA_ERR_SHAPE;  // one head's N x N bias must span < 2^32 bytes
+  if (bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
+  const void* ptrs[] = {q, k, v, bias, o, lse};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if (N % 8 != 0 || bias_stride_b % 8 != 0 || bias_stride_h % 8 != 0) return FA_ERR_ALIGN;
+  fa::FwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = B * H;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  p.bias = bias;
+  p.bias_sb = bias_stride_b;
+  p.bias_sh = bias_stride_h;
+  return fa::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
   if (num_splits < 1 || num_splits > 64) return 0;

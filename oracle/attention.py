@@ -48,15 +48,19 @@ def _visible_mask(n_q: int, n_k: int, causal: bool) -> np.ndarray | None:
 
 
 def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                 causal: bool) -> Tuple[np.ndarray, np.ndarray]:
+                 causal: bool, bias: np.ndarray | None = None) -> Tuple[np.ndarray, np.ndarray]:
     """One (batch, head): q,k,v float64 [N, d] -> (O [N, d], LSE [N]).
 
-    Materialises S = scale * Q K^T, masks, and takes a max-subtracted softmax
-    over each row (page 1 examples 1-3; page 2 "Kernel Fusion" baseline).
-    A row with no visible key (unreachable when key 0 is always visible) gets
-    O = 0 and LSE = -inf.
+    Materialises S = scale * Q K^T (+ bias [N, N], an additive attention bias
+    in the same natural-log units; page 2, "工程落地的关键考量", suggests one
+    for masking very long sequences), masks, and takes a max-subtracted
+    softmax over each row (page 1 examples 1-3; page 2 "Kernel Fusion"
+    baseline).  A row with no visible key or only -inf scores gets O = 0 and
+    LSE = -inf.
     """
     s = scale * (q @ k.T)
+    if bias is not None:
+        s = s + bias
     vis = _visible_mask(q.shape[0], k.shape[0], causal)
     if vis is not None:
         s = np.where(vis, s, -np.inf)
@@ -71,14 +75,17 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-            causal: bool) -> Tuple[np.ndarray, np.ndarray]:
-    """[B, H, N, d] float64 -> (O [B, H, N, d], LSE [B, H, N]), one head at a time."""
+            causal: bool, bias: np.ndarray | None = None) -> Tuple[np.ndarray, np.ndarray]:
+    """[B, H, N, d] float64 -> (O [B, H, N, d], LSE [B, H, N]), one head at a time.
+    ``bias`` (optional) broadcasts to [B, H, N, N]."""
     B, H, N, d = q.shape
     o = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
+    bb = None if bias is None else np.broadcast_to(bias, (B, H, N, k.shape[2]))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, causal,
+                                              None if bb is None else bb[b, h])
     return o, lse
 
 
@@ -104,10 +111,11 @@ def forward_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Iterable,
     return out_o, out_lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool):
+def backward_head(q, k, v, do, scale: float, causal: bool, bias=None):
     """Gradients of L = <dO, O> for one head; inputs float64 [N, d].
 
-    With P the normalised softmax of S = scale * Q K^T (masked):
+    With P the normalised softmax of S = scale * Q K^T (+ bias, a constant
+    whose gradient dS is not formed here) (masked):
         dV = P^T dO
         dP = dO V^T
         D_i = sum_j P_ij dP_ij            (equals sum_c dO_ic O_ic)
@@ -115,12 +123,17 @@ def backward_head(q, k, v, do, scale: float, causal: bool):
         dQ = scale * dS K,   dK = scale * dS^T Q
     """
     s = scale * (q @ k.T)
+    if bias is not None:
+        s = s + bias
     vis = _visible_mask(q.shape[0], k.shape[0], causal)
     if vis is not None:
         s = np.where(vis, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
     p = np.exp(s - m)
-    p /= p.sum(axis=1, keepdims=True)
+    l = p.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        p = np.where(l > 0, p / l, 0.0)  # a row with every score -inf has O = 0
     dv = p.T @ do
     dp = do @ v.T
     dsum = (p * dp).sum(axis=1, keepdims=True)
@@ -130,16 +143,19 @@ def backward_head(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
-def backward(q, k, v, do, scale: float, causal: bool):
-    """[B, H, N, d] float64 -> (dQ, dK, dV), one head at a time."""
+def backward(q, k, v, do, scale: float, causal: bool, bias=None):
+    """[B, H, N, d] float64 -> (dQ, dK, dV), one head at a time.
+    ``bias`` (optional) broadcasts to [B, H, N, N]."""
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    B, H = q.shape[:2]
+    B, H, N = q.shape[:3]
+    bb = None if bias is None else np.broadcast_to(bias, (B, H, N, k.shape[2]))
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = backward_head(
-                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+                q[b, h], k[b, h], v[b, h], do[b, h], scale, causal,
+                None if bb is None else bb[b, h])
     return dq, dk, dv
 
 

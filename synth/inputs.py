@@ -38,8 +38,8 @@ def f32_to_bits(x: np.ndarray, fmt: str) -> np.ndarray:
         return x.astype(np.float16).view(np.uint16)
     if fmt == FMT_BF16:
         u = x.view(np.uint32).astype(np.uint64)
-        if np.any((u & 0x7F800000) == 0x7F800000):
-            raise ValueError("non-finite value in bf16 input generation")
+        if np.any(((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)):
+            raise ValueError("NaN in bf16 input generation")  # +-inf round to themselves
         rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
         return rounded.astype(np.uint16)
     raise ValueError(f"unknown format {fmt!r}")
@@ -161,6 +161,41 @@ def long_causal(N: int = 32768, with_do: bool = False) -> Workload:
     t = _draw([4, N], shape, 0.5, FMT_BF16, with_do)
     return Workload(f"long_causal_B1H8N{N}d64_bf16", *shape, FMT_BF16, True, default_scale(64),
                     t["q"], t["k"], t["v"], t.get("do"))
+
+
+def attn_bias(shape, fmt: str, seed, kind: str = "random", **kw) -> np.ndarray:
+    """Seeded additive attention bias bits of ``shape`` (..., N, N), 16-bit.
+
+    kinds:
+      "random": N(0, std^2) (std = kw "std", default 2) with a fraction
+                kw "hole" (default 0.2) of entries set to -inf, and row
+                kw "dead_row" (default 3, if < N) entirely -inf.
+      "window": 0 where |i - j| <= kw "width", -inf elsewhere (a band).
+      "keypad": 0 for keys j < L_b, -inf beyond, with L_b from kw "lengths"
+                (one per leading index of ``shape``).
+    """
+    shape = tuple(shape)
+    n_q, n_k = shape[-2], shape[-1]
+    if kind == "random":
+        rng = np.random.default_rng(list(seed) + [7])
+        x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(kw.get("std", 2.0)))
+        x[rng.random(shape) < kw.get("hole", 0.2)] = -np.inf
+        r = kw.get("dead_row", 3)
+        if r is not None and r < n_q:
+            x[..., r, :] = -np.inf
+    elif kind == "window":
+        i = np.arange(n_q)[:, None]
+        j = np.arange(n_k)[None, :]
+        band = np.where(np.abs(i - j) <= kw["width"], 0.0, -np.inf).astype(np.float32)
+        x = np.broadcast_to(band, shape).copy()
+    elif kind == "keypad":
+        lengths = list(kw["lengths"])
+        x = np.zeros(shape, dtype=np.float32)
+        for b, L in enumerate(lengths):
+            x[b, ..., L:] = -np.inf
+    else:
+        raise ValueError(kind)
+    return f32_to_bits(x, fmt)
 
 
 def long_causal_sample_rows(H: int, N: int, count: int = 256):

@@ -27,7 +27,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "flash_attn_fwd", "flash_attn_fwd_splitkv", "flash_attn_fwd_splitkv_workspace_bytes",
+        "flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv",
+        "flash_attn_fwd_splitkv_workspace_bytes",
         "flash_attn_fwd_splitkv_default_splits", "flash_attn_bwd", "flash_attn_bwd_preprocess",
         "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
         "flash_attn_status_string", "flash_attn_version"])
@@ -178,3 +179,15 @@ def test_fwd_splitkv_validation(lib, kw, status):
                 d=64, scale=0.125, causal=0, dtype=0, num_splits=2, stream=None)
     args.update(kw)
     assert lib.flash_attn_fwd_splitkv(**args) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bias=None), 1), (dict(q=None), 1), (dict(N=0), 2), (dict(N=46344), 2), (dict(d=32), 3),
+    (dict(dtype=6), 4), (dict(bias=P + 2), 5), (dict(N=12), 5), (dict(bias_stride_b=4), 5),
+    (dict(bias_stride_h=12), 5), (dict(bias_stride_b=-8), 2), (dict(scale=0.0), 8),
+])
+def test_fwd_bias_validation(lib, kw, status):
+    args = dict(q=P, k=P, v=P, bias=P, bias_stride_b=0, bias_stride_h=64, o=P, lse=P, B=1, H=1,
+                N=8, d=64, scale=0.125, causal=0, dtype=0, stream=None)
+    args.update(kw)
+    assert lib.flash_attn_fwd_bias(**args) == status

@@ -392,6 +392,68 @@ def test_sampled_gradients_finite_difference():
 
 
 # ----------------------------------------------------------------------------
+# Additive attention bias
+# ----------------------------------------------------------------------------
+def test_bias_special_cases():
+    """Zero bias is no bias; a bias constant along each row leaves O unchanged
+    and adds that constant to LSE; -inf above the diagonal is the causal mask;
+    a bias of log(w_j) reweights the softmax by w_j (checked against a direct
+    weighted average); a row of -inf gives O = 0, LSE = -inf."""
+    N, d, sc = 9, 4, 0.6
+    q, k, v = rand((N, d), 90), rand((N, d), 91), rand((N, d), 92)
+    o0, l0 = oracle.forward_head(q, k, v, sc, False)
+    o, l = oracle.forward_head(q, k, v, sc, False, np.zeros((N, N)))
+    np.testing.assert_allclose(o, o0, atol=1e-14)
+    np.testing.assert_allclose(l, l0, atol=1e-14)
+    rowc = rand((N, 1), 93)
+    o, l = oracle.forward_head(q, k, v, sc, False, np.repeat(rowc, N, axis=1))
+    np.testing.assert_allclose(o, o0, atol=1e-13)
+    np.testing.assert_allclose(l, l0 + rowc[:, 0], atol=1e-13)
+    tri = np.where(np.tri(N) > 0, 0.0, -np.inf)
+    oc, lc = oracle.forward_head(q, k, v, sc, True)
+    o, l = oracle.forward_head(q, k, v, sc, False, tri)
+    np.testing.assert_allclose(o, oc, atol=1e-14)
+    np.testing.assert_allclose(l, lc, atol=1e-14)
+    w = np.abs(rand((N,), 94)) + 0.1
+    o, l = oracle.forward_head(q, k, v, sc, False, np.log(np.broadcast_to(w, (N, N))))
+    e = np.exp(sc * (q @ k.T)) * w
+    np.testing.assert_allclose(o, (e @ v) / e.sum(axis=1, keepdims=True), atol=1e-12)
+    np.testing.assert_allclose(l, np.log(e.sum(axis=1)), atol=1e-12)
+    hole = np.zeros((N, N))
+    hole[3] = -np.inf
+    o, l = oracle.forward_head(q, k, v, sc, True, hole)
+    assert np.all(o[3] == 0) and l[3] == -np.inf
+    np.testing.assert_allclose(np.delete(o, 3, 0), np.delete(oc, 3, 0), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_gradients_finite_difference(causal):
+    """Gradients with a bias (including -inf entries and one fully hidden row):
+    central differences of <dO, O> in Q, K and V."""
+    B, H, N, d, sc, h = 1, 1, 6, 3, 0.5, 1e-6
+    q, k, v, do = (rand((B, H, N, d), s) for s in (95, 96, 97, 98))
+    bias = rand((N, N), 99)
+    bias[1, 4] = -np.inf
+    bias[2] = -np.inf
+    dq, dk, dv = oracle.backward(q, k, v, do, sc, causal, bias)
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward(q_, k_, v_, sc, causal, bias)
+        return float((o * do).sum())
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p, args_m = [q, k, v], [q, k, v]
+            pos = "qkv".index(name)
+            args_p[pos], args_m[pos] = xp, xm
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.linalg.norm(fd - g) <= 1e-6 * max(np.linalg.norm(fd), 1e-12), name
+    assert np.all(dq[0, 0, 2] == 0)
+
+
+# ----------------------------------------------------------------------------
 # Input generator and tolerance feasibility
 # ----------------------------------------------------------------------------
 def test_rounding_formats():

@@ -246,3 +246,72 @@ def test_splitkv_long_causal_sampled():
     o, lse = run_splitkv(w, 16)
     rows = [(0, int(h), int(i)) for h, i in si.long_causal_sample_rows(w.H, w.N)]
     check(w, o, lse, rows=rows, tag=" splits=16")
+
+
+# ----------------------------------------------------------------------------
+# additive attention bias
+# ----------------------------------------------------------------------------
+def run_bias(w, bias_bits, out_f32=False):
+    import torch
+    import io_aware_exact_08_amd as fa
+    from gpu_helpers import to_dev
+    q, k, v = dev_inputs(w)[:3]
+    bias = to_dev(bias_bits, w.fmt)
+    o, lse = fa.flash_attn_fwd_bias(q, k, v, bias, causal=w.causal, scale=w.scale,
+                                    out_f32=out_f32)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_bias(w, bias_bits, o, lse, tag=""):
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    bias = si.bits_to_f64(bias_bits, w.fmt)
+    o_ref, l_ref = oracle.forward(q, k, v, w.scale, w.causal, bias)
+    og, lg = f64(o), f64(lse)
+    dead = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(lg), dead), "rows with every key hidden must give LSE = -inf"
+    assert np.all(og[dead] == 0.0), "rows with every key hidden must give O = 0"
+    live = ~dead
+    eo = np.abs(og[live] - o_ref[live]).max() if live.any() else 0.0
+    el = np.abs(lg[live] - l_ref[live]).max() if live.any() else 0.0
+    gated = gated_o_error(og[live], o_ref[live], str(o.dtype) == "torch.bfloat16") if live.any() else 0.0
+    print(f"{w.name}{tag}: max|dO|={eo:.3e} max|dLSE|={el:.3e} hidden rows={int(dead.sum())}",
+          flush=True)
+    assert np.isfinite(og).all()
+    assert gated <= TOL_O[w.fmt] and el <= TOL_LSE, (eo, gated, el)
+
+
+@pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, True)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [8, 64, 200, 520])
+@pytest.mark.parametrize("layout", ["shared", "per_head", "per_batch_head"])
+def test_bias_random(N, d, causal, fmt, out_f32, layout):
+    """Random N(0, 2^2) bias with 20% of entries -inf and one row fully hidden,
+    broadcast as [N, N], [H, N, N] or stored as [B, H, N, N]."""
+    w = si.random_case(2, 2, N, d, fmt, causal, seed=5 * N + d)
+    shape = {"shared": (N, N), "per_head": (2, N, N), "per_batch_head": (2, 2, N, N)}[layout]
+    bb = si.attn_bias(shape, fmt, [N, d, len(shape)], "random")
+    o, lse = run_bias(w, bb, out_f32=out_f32)
+    check_bias(w, bb, o, lse, tag=f" {layout}")
+
+
+def test_bias_zero_equals_plain_forward():
+    import torch
+    w = si.random_case(1, 3, 256, 64, si.FMT_F16, False, seed=21)
+    zero = np.zeros((256, 256), dtype=np.uint16)
+    o, lse = run_bias(w, zero)
+    o0, l0 = run_fwd(w)
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+
+
+@pytest.mark.parametrize("kind,kw", [("window", dict(width=100)), ("keypad", dict(lengths=[300, 2048]))])
+def test_bias_masks_long(kind, kw):
+    """Sliding-window band and per-batch key padding at N=2048 (B=2 H=2 d=64
+    fp16), every element; the window keeps each row 201 keys, the padding
+    hides keys past 300 in batch 0."""
+    w = si.random_case(2, 2, 2048, 64, si.FMT_F16, False, seed=33)
+    bb = si.attn_bias((2, 1, 2048, 2048) if kind == "keypad" else (2048, 2048), w.fmt, [33], kind,
+                      **kw)
+    o, lse = run_bias(w, bb)
+    check_bias(w, bb, o, lse, tag=f" {kind}")
