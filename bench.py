@@ -149,11 +149,29 @@ def config_sweep(fa, si, torch, np, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    def run(name, w, out_f32=False, bwd=False, reps=20, splits=None):
+    def run(name, w, out_f32=False, bwd=False, reps=20, splits=None, bias_bits=None):
         q, k, v, do = tensors(w)
         B, H, N, d = w.shape
         fl = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         o, lse = fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out_f32=out_f32)
+        if bias_bits is not None:
+            dt = torch.float16 if w.fmt == "f16" else torch.bfloat16
+            bias = torch.from_numpy(bias_bits.view(np.int16)).view(dt).to(dev)
+            ms = timed(lambda: fa.flash_attn_fwd_bias(q, k, v, bias, causal=w.causal, scale=w.scale,
+                                                      out_f32=out_f32, o=o, lse=lse), reps)
+            rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal, "bias": list(bias.shape),
+                   "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+            if bwd:
+                ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32,
+                                 device=dev)
+                dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+                ms_b = timed(lambda: fa.flash_attn_bwd_bias(q, k, v, bias, o, lse, do,
+                                                            causal=w.causal, scale=w.scale, dq=dq,
+                                                            dk=dk, dv=dv, workspace=ws), reps)
+                rec["bwd_ms"] = round(ms_b, 4)
+                rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
+            out[name] = rec
+            return
         if splits is None:
             ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
                                                  out_f32=out_f32, o=o, lse=lse), reps)
@@ -188,6 +206,8 @@ def config_sweep(fa, si, torch, np, dev):
     run("fwd_B1H4N8192d128_bf16", few, out_f32=True)
     run("fwd_splitkv_B1H4N8192d128_bf16", few, out_f32=True, splits=0)
     run("fwdbwd_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True)
+    run("fwdbwd_bias_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True,
+        bias_bits=si.attn_bias((2, 12, 4096, 4096), "f16", [5, 4096], "random", hole=0.1))
     run("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), bwd=True)
     return out
 

@@ -106,6 +106,20 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    void* stream);
 
 /*
+ * Backward of flash_attn_fwd_bias: the same gradients of L = <dO, O> with
+ * P_ij = exp(scale * q_i . k_j + bias_ij - LSE_i) rebuilt from the bias and
+ * the LSE flash_attn_fwd_bias wrote (the bias is a constant: its own
+ * gradient, dS, is not formed).  Rows whose every key is hidden contribute
+ * nothing.  Arguments as flash_attn_bwd, plus bias and its strides exactly as
+ * passed to flash_attn_fwd_bias (same checks).
+ */
+int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                        long long bias_stride_b, long long bias_stride_h, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                        float scale, int causal, int dtype, void* stream);
+
+/*
  * The three stages of flash_attn_bwd, callable on their own (same arguments,
  * layouts and checks as flash_attn_bwd; flash_attn_bwd is exactly these three
  * in order on one stream).  dK/dV and dQ only read the workspace the

@@ -7,6 +7,7 @@ module only marshals torch tensors (device memory and streams) into its C ABI:
     flash_attn_fwd_bias(q, k, v, bias, causal=False, scale=None) -> (o, lse)
     flash_attn_fwd_splitkv(q, k, v, causal=False, scale=None, num_splits=0) -> (o, lse)
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
+    flash_attn_bwd_bias(q, k, v, bias, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
 
 Layout [B, H, N, d], d in {64, 128}, fp16 or bf16 inputs.
 """
@@ -17,7 +18,8 @@ import math
 from . import _lib
 from ._lib import FlashAttnError, status_string  # noqa: F401
 
-__all__ = ["flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+__all__ = ["flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv", "flash_attn_bwd",
+           "flash_attn_bwd_bias", "flash_attn_bwd_preprocess",
            "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "FlashAttnError", "status_string",
            "dtype_code", "workspace_bytes"]
 
@@ -185,6 +187,39 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None,
                              B, H, N, d, sc, int(bool(causal)), code, _stream(q))
     if st != _lib.FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def flash_attn_bwd_bias(q, k, v, bias, o, lse, dout, causal: bool = False, scale=None,
+                        dq=None, dk=None, dv=None, workspace=None):
+    """Backward of flash_attn_fwd_bias (same bias): returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    if not bias.is_cuda or bias.dtype != q.dtype:
+        raise TypeError("bias must be a device tensor of the input dtype")
+    bb = bias.expand(B, H, N, N)
+    if bb.stride(3) != 1 or bb.stride(2) != N:
+        raise ValueError("bias rows must be contiguous [N, N] blocks")
+    out_f32 = o.dtype == torch.float32
+    _check(o, "o", (B, H, N, d), o.dtype)
+    _check(lse, "lse", (B, H, N), torch.float32)
+    code = dtype_code(q.dtype, out_f32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=q.device)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_bwd_bias(q.data_ptr(), k.data_ptr(), v.data_ptr(), bb.data_ptr(),
+                                  bb.stride(0), bb.stride(1), o.data_ptr(), lse.data_ptr(),
+                                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  B, H, N, d, sc, int(bool(causal)), code, _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_bias")
     return dq, dk, dv
 
 

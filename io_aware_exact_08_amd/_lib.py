@@ -22,6 +22,7 @@ EXPORTED = (
     "flash_attn_fwd_splitkv_workspace_bytes",
     "flash_attn_fwd_splitkv_default_splits",
     "flash_attn_bwd",
+    "flash_attn_bwd_bias",
     "flash_attn_bwd_preprocess",
     "flash_attn_bwd_dkdv",
     "flash_attn_bwd_dq",
@@ -64,6 +65,9 @@ def load() -> ctypes.CDLL:
     lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    i, i, i, i, f, i, i, vp]
     lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_bias.argtypes = [vp, vp, vp, vp, ll, ll, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_bias.restype = i
     lib.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
     lib.flash_attn_bwd_preprocess.restype = i
     lib.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, i, vp]
@@ -119,6 +123,14 @@ def flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes
     return load().flash_attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace,
                                  workspace_bytes, B, H, N, d, float(scale), int(causal),
                                  int(dtype), stream)
+
+
+def flash_attn_bwd_bias(q, k, v, bias, bias_stride_b, bias_stride_h, o, lse, dout, dq, dk, dv,
+                        workspace, workspace_bytes, B, H, N, d, scale, causal, dtype, stream) -> int:
+    """Raw C call with integer device pointers; returns the fa_status."""
+    return load().flash_attn_bwd_bias(q, k, v, bias, int(bias_stride_b), int(bias_stride_h), o, lse,
+                                      dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                                      float(scale), int(causal), int(dtype), stream)
 
 
 def flash_attn_bwd_preprocess(o, lse, dout, workspace, workspace_bytes, B, H, N, d, dtype,

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __rest
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w, 64);
   if (row < rows && c == 0) {
     delta[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    // a row whose every key is hidden (LSE = -inf, O = 0) must recompute P = 0
+    lse2[row] = lse[row] == -INFINITY ? INFINITY : lse[row] * kLog2e;
   }
 }
 
@@ -96,6 +97,10 @@ struct BwdArgs {
   int n_tiles;  // workgroup tiles per head
   float c;      // scale * log2(e)
   float scale;
+  // additive attention bias (as in the forward), or null
+  const uint16_t* bias;
+  long long bias_sb, bias_sh;
+  int H;
 };
 
 // Per-lane byte offsets shared by both kernels for a row-major LDS tile with
@@ -157,8 +162,12 @@ template <int D>
 __host__ __device__ constexpr int dkdv_stage_bytes() {
   return 2 * kDkvBQ * D * 2 + 2 * kDkvBQ * 4;  // Q, dO tiles + LSE2, D rows
 }
+// With an attention bias a stage also holds the bias block of the tile's 64
+// query rows x the workgroup's 128 keys (row-major, 256 bytes per row).
+constexpr int kDkvBiasRowBytes = kDkvKeys * 2;
+constexpr int kDkvBiasBytes = kDkvBQ * kDkvBiasRowBytes;
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BQ = kDkvBQ;
   constexpr int DC = D / 16;
@@ -169,8 +178,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   constexpr int ROWB = D * 2;
   constexpr int LOADS = BQ * CPR / kBwdThreads;
   static_assert(LOADS * kBwdThreads == BQ * CPR, "tile split");
-  constexpr int STAGE = dkdv_stage_bytes<D>();
+  constexpr int STAGE = dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
+  constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -197,6 +207,17 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
   const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
   const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
+  const brsrc_t rb =
+      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
+                BIAS ? (uint32_t)N * N * 2 : 0u);
+  // Bias gather through the transposing read: in each 16-lane group (G), lane
+  // L supplies row R + L/4 and columns c0 + 4(L%4) .. +3 of the row-major bias
+  // block; result lane i then holds rows R..R+3 of column c0 + i.  With
+  // c0 = 32*wave + 16(G%2) and R = 32t + 16g + 8(G/2) (+4), lane l receives
+  // exactly the bias of its key (32*wave + l%32) at the query rows of score
+  // registers 8g + 0..3 (and 4..7) of sub-tile t.
+  const int bias_rd = ((lane & 15) >> 2) * kDkvBiasRowBytes + 8 * ((lane >> 5) & 1) * kDkvBiasRowBytes +
+                      (32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   const int kw0 = kvt * kDkvKeys + wave * 32;  // first key of this wave
   const int key = kw0 + m;                     // this lane's key (column of S)
 
@@ -240,6 +261,17 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
       if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
     }
+    if constexpr (BIAS) {
+      // bias rows qt*BQ .. +63, columns of this workgroup's 128 keys: slot p
+      // holds row p/16, 16-byte chunk p%16 (rows past N read as 0)
+#pragma unroll
+      for (int i = 0; i < kDkvBiasBytes / 16 / kBwdThreads; ++i) {
+        const int p = i * kBwdThreads + tid;
+        const uint32_t off =
+            (uint32_t)(((qt * BQ + p / 16) * N + kvt * kDkvKeys + (p % 16) * 8) * 2);
+        bload16_lds(rb, stage + BIAS_OFF + (i * kBwdThreads + wave * 64) * 16, off, 0u);
+      }
+    }
   };
 
   const float c = a.c;
@@ -273,6 +305,25 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
         s[t] = mfma32<BF16>(qa, kf[dc], s[t]);
         dp[t] = mfma32<BF16>(ga, vf[dc], dp[t]);
       }
+    }
+    if constexpr (BIAS) {
+      // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e))
+      const float kb = 1.0f / a.scale;
+      const char* sB = stage + BIAS_OFF;
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const u32x2 w = lds_read_tr16(sB + bias_rd + (t * 32 + 16 * g + 4 * half) * kDkvBiasRowBytes);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 8 * g + 4 * half + 2 * e;
+              s[t][r] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w[e] & 0xffffu)), kb, s[t][r]);
+              s[t][r + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w[e] >> 16)), kb, s[t][r + 1]);
+            }
+          }
     }
     u32x4 pp[QC], ps[QC];
 #pragma unroll
@@ -370,7 +421,7 @@ __host__ __device__ constexpr int dq_stage_bytes() {
   return 2 * kDqBK * D * 2;  // K, V tiles
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BK = kDqBK;
   constexpr int DC = D / 16;
@@ -409,6 +460,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
   const int qw0 = qt * kDqRows + wave * 32;
   const int qrow = qw0 + m;
+  const brsrc_t rb =
+      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
+                BIAS ? (uint32_t)N * N * 2 : 0u);
 
   // Q^T and dO^T as B operands (lane: query m; slot i: d = 16dc + 8h + i).
   u32x4 qf[DC], gf[DC];
@@ -460,6 +514,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     const char* sV = stage + TILE;
     // S^T = K Q^T, dP^T - D = V dO^T - D (rows: keys with perm_k, cols:
     // queries).  Register r of key tile kt holds key kt*32 + 16(r/8) + 8h + r%8.
+    // With a bias, registers 8g..8g+7 of key tile kt need eight consecutive
+    // entries of this lane's bias row: one 16-byte load each, issued first.
+    u32x4 bw[KT][2];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          bw[kt][g] = bload16(rb, (uint32_t)((qrow * N + k0 + 32 * kt + 16 * g + 8 * h) * 2), 0);
+    }
     f32x16 s[KT], dp[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -474,6 +538,19 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
         dp[kt] = mfma32<BF16>(va, gf[dc], dp[kt]);
       }
     }
+    if constexpr (BIAS) {
+      const float kb = 1.0f / a.scale;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = bw[kt][g][e];
+            s[kt][8 * g + 2 * e] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w & 0xffffu)), kb, s[kt][8 * g + 2 * e]);
+            s[kt][8 * g + 2 * e + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w >> 16)), kb, s[kt][8 * g + 2 * e + 1]);
+          }
+    }
     u32x4 ps[KC];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -482,8 +559,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[kt][r], c, -lse2));
         if constexpr (MASK) {
+          // causal diagonal; with a bias also keys past N, whose bias entries
+          // are read from the next row and must not reach dS
           const int keyi = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-          if (keyi > qrow) p = 0.f;
+          if ((CAUSAL && keyi > qrow) || (BIAS && keyi >= a.N)) p = 0.f;
         }
         dsv[r] = p * dp[kt][r];
       }
@@ -510,7 +589,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     const int k0 = j * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 31);
     if (active) {
-      if (CAUSAL && k0 + BK - 1 > qw0) {
+      if ((CAUSAL && k0 + BK - 1 > qw0) || (BIAS && k0 + BK > a.N)) {
         tile_body(std::true_type{}, cur, k0);
       } else {
         tile_body(std::false_type{}, cur, k0);
@@ -555,6 +634,10 @@ static hipError_t set_lds(Kern kern, int bytes) {
 
 static BwdArgs make_args(const BwdProblem& p) {
   BwdArgs a;
+  a.bias = (const uint16_t*)p.bias;
+  a.bias_sb = p.bias_sb;
+  a.bias_sh = p.bias_sh;
+  a.H = p.H;
   a.q = (const uint16_t*)p.q;
   a.k = (const uint16_t*)p.k;
   a.v = (const uint16_t*)p.v;
@@ -582,24 +665,24 @@ static hipError_t launch_pre_t(const BwdProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool BIAS>
 static hipError_t launch_dkdv_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
-  const int lds = 2 * dkdv_stage_bytes<D>();
-  auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL>;
+  const int lds = 2 * (dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0));
+  auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool BIAS>
 static hipError_t launch_dq_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
   const int lds = 2 * dq_stage_bytes<D>();
-  auto kern = bwd_dq_kernel<D, BF16, CAUSAL>;
+  auto kern = bwd_dq_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
@@ -627,11 +710,15 @@ struct PreL {
 };
 template <int D, bool BF16, bool X>
 struct DkdvL {
-  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_dkdv_t<D, BF16, X>(p, s); }
+  static hipError_t run(const BwdProblem& p, hipStream_t s) {
+    return p.bias ? launch_dkdv_t<D, BF16, X, true>(p, s) : launch_dkdv_t<D, BF16, X, false>(p, s);
+  }
 };
 template <int D, bool BF16, bool X>
 struct DqL {
-  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_dq_t<D, BF16, X>(p, s); }
+  static hipError_t run(const BwdProblem& p, hipStream_t s) {
+    return p.bias ? launch_dq_t<D, BF16, X, true>(p, s) : launch_dq_t<D, BF16, X, false>(p, s);
+  }
 };
 
 hipError_t launch_bwd_pre(const BwdProblem& p, hipStream_t s) {

@@ -46,6 +46,9 @@ struct BwdProblem {
   float scale;
   bool causal;
   int dtype;
+  int H = 1;                   // heads per batch entry (bias addressing)
+  const void* bias = nullptr;  // additive attention bias, or null
+  long long bias_sb = 0, bias_sh = 0;
 };
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t stream);

@@ -173,6 +173,46 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
+                        long long bias_stride_b, long long bias_stride_h, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                        float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (N > 46340 || bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, bias, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if (N % 8 != 0 || bias_stride_b % 8 != 0 || bias_stride_h % 8 != 0) return FA_ERR_ALIGN;
+  fa::BwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = (float*)workspace;
+  p.lse2 = (float*)workspace + (size_t)B * H * N;
+  p.BH = B * H;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  p.bias = bias;
+  p.bias_sb = bias_stride_b;
+  p.bias_sh = bias_stride_h;
+  return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 // Shared checks of the three backward stages; fills p (pointers not listed
 // for a stage are left NULL).
 static int bwd_stage_setup(fa::BwdProblem& p, const void* workspace, size_t workspace_bytes, int B,

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv",
         "flash_attn_fwd_splitkv_workspace_bytes",
-        "flash_attn_fwd_splitkv_default_splits", "flash_attn_bwd", "flash_attn_bwd_preprocess",
+        "flash_attn_fwd_splitkv_default_splits", "flash_attn_bwd", "flash_attn_bwd_bias",
+        "flash_attn_bwd_preprocess",
         "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
         "flash_attn_status_string", "flash_attn_version"])
 
@@ -191,3 +192,17 @@ def test_fwd_bias_validation(lib, kw, status):
                 N=8, d=64, scale=0.125, causal=0, dtype=0, stream=None)
     args.update(kw)
     assert lib.flash_attn_fwd_bias(**args) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bias=None), 1), (dict(dv=None), 1), (dict(N=0), 2), (dict(N=46344), 2),
+    (dict(bias_stride_h=-8), 2), (dict(d=48), 3), (dict(dtype=9), 4), (dict(bias=P + 8), 5),
+    (dict(N=20), 5), (dict(bias_stride_b=12), 5), (dict(workspace=None), 7),
+    (dict(workspace_bytes=8 * 8 - 1), 7), (dict(scale=float("inf")), 8),
+])
+def test_bwd_bias_validation(lib, kw, status):
+    args = dict(q=P, k=P, v=P, bias=P, bias_stride_b=64, bias_stride_h=0, o=P, lse=P, dout=P,
+                dq=P, dk=P, dv=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1, N=8, d=64,
+                scale=0.125, causal=0, dtype=0, stream=None)
+    args.update(kw)
+    assert lib.flash_attn_bwd_bias(**args) == status
