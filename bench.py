@@ -209,6 +209,9 @@ def config_sweep(fa, si, torch, np, dev):
     run("fwdbwd_bias_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True,
         bias_bits=si.attn_bias((2, 12, 4096, 4096), "f16", [5, 4096], "random", hole=0.1))
     run("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), bwd=True)
+    run("fwd_B2H8N4096d256_f16", si.random_case(2, 8, 4096, 256, "f16", False, seed=257))
+    run("fwd_causal_B2H8N4096d256_bf16_f32out", si.random_case(2, 8, 4096, 256, "bf16", True, seed=257),
+        out_f32=True)
     return out
 
 

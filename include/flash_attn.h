@@ -22,8 +22,11 @@
  *    surface at the caller's next synchronisation.
  *  - Errors: the return value is a fa_status.  Arguments are validated before
  *    anything is enqueued; on a non-zero status nothing was launched.
- *  - Sizes: B, H, N >= 1, any N (tail tiles are masked); d in {64, 128};
- *    B*H*N*d < 2^31 elements per tensor.
+ *  - Sizes: B, H, N >= 1, any N (tail tiles are masked); head dimension d in
+ *    {64, 128, 256} for the forward entry points and {64, 128} for the
+ *    backward ones (page 2, "工程落地的关键考量", hardware
+ *    requirements, names 64, 128 and 256 as the preferred head sizes; no
+ *    d=256 backward is provided); B*H*N*d < 2^31 elements per tensor.
  *  - Causal: key j is visible to query i iff j <= i (queries and keys share the
  *    same length N).
  *  - Arithmetic: fp16 or bf16 operands, float32 accumulation and softmax state,
@@ -43,7 +46,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL                       */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 elements  */
-  FA_ERR_HEADDIM = 3,   /* d not in {64, 128}                               */
+  FA_ERR_HEADDIM = 3,   /* d not in {64,128,256} (fwd) or {64,128} (bwd)    */
   FA_ERR_DTYPE = 4,     /* unknown fa_dtype                                 */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                 */
   FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */

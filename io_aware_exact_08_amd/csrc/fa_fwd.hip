@@ -74,16 +74,36 @@ template <>
 struct FwdCfg<64> {
   static constexpr int QB = FA_FWD64_QB;  // 32-row query blocks per wave
   static constexpr int BK = FA_FWD64_BK;  // keys per tile
+  static constexpr int STAGES = FA_FWD_STAGES;        // K/V tiles resident in LDS
+  static constexpr bool Q_LDS = false;                // Q^T operand from LDS (else registers)
+  static constexpr int MIN_WAVES = FA_FWD_MIN_WAVES;  // waves per SIMD the registers allow
 };
 template <>
 struct FwdCfg<128> {
   static constexpr int QB = 1;
   static constexpr int BK = 32;
+  static constexpr int STAGES = FA_FWD_STAGES;
+  static constexpr bool Q_LDS = false;
+  static constexpr int MIN_WAVES = FA_FWD_MIN_WAVES;
+};
+// d=256: the O^T accumulators alone take 128 registers per lane, so the Q^T
+// operand is read from LDS instead of being held in 64 more (with it in
+// registers the accumulators no longer fit in VGPRs, and every online-softmax
+// rescale of AGPR-resident accumulators spills).  Q (64 KB) plus three 32-key
+// stages of K and V (96 KB) fill the CU's 160 KB of LDS: one workgroup per CU,
+// one wave per SIMD.  MFMA work per key tile is 4x that of d=64 while the
+// softmax work is the same, so that single wave keeps the matrix core busy.
+template <>
+struct FwdCfg<256> {
+  static constexpr int QB = 1;
+  static constexpr int BK = 32;
+  static constexpr int STAGES = 3;
+  static constexpr bool Q_LDS = true;
+  static constexpr int MIN_WAVES = 1;
 };
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = FA_FWD_STAGES;  // K/V tiles resident in LDS (>= 2)
 
 // Lazy-rescale threshold (log2 units).  bf16 keeps the exact running max
 // (threshold 0): the dominant probability is then exactly 1 and is not
@@ -118,7 +138,7 @@ struct FwdArgs {
 };
 
 template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV, bool BIAS>
-__global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(FwdArgs a) {
   constexpr int QB = FwdCfg<D>::QB;
   constexpr int BK = FwdCfg<D>::BK;
   constexpr int BQ = kWaves * QB * 32;
@@ -130,12 +150,20 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   constexpr int ROWB = D * 2;  // bytes per K/V row
   constexpr int LOADS = BK * CPR / kThreads;  // 16-byte slots per thread per tile
   static_assert(LOADS * kThreads == BK * CPR, "tile split");
+  constexpr int kStages = FwdCfg<D>::STAGES;
+  static_assert(kStages == 3 || kStages == 4, "the pipeline below runs three or four stages");
+  constexpr bool Q_LDS = FwdCfg<D>::Q_LDS;
+  static_assert(!Q_LDS || QB == 1, "LDS-resident Q assumes one query block per wave");
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[kStages][BK * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kStages][BK * D];
+  // the workgroup's Q tile, row-major and swizzled like K (Q_LDS only)
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[Q_LDS ? BQ * D : 8];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // (wave-uniform for the LDS-resident Q path, which then addresses its DMA
+  // bases from scalar registers; the other paths measured better without)
+  const int wave = Q_LDS ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int lane = tid & 63;
   const int m = lane & 31;
   const int h = lane >> 5;
@@ -170,35 +198,65 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
                 BIAS ? (uint32_t)N * N * 2 : 0u);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query m, half h), slot i
-  // holds d = 16*dc + 8*h + i.  Rows past N read as 0.
-  u32x4 qf[QB][DC];
+  // holds d = 16*dc + 8*h + i.  Rows past N read as 0.  With Q_LDS they are
+  // read from sQ on every key tile instead (q_rd: this lane's chunk offsets in
+  // its wave's 32 rows; rows are 16-byte-chunk swizzled so the 16 lanes of a
+  // read cycle hit distinct bank slots).
+  // The swizzles permute 16-byte chunks only within a 256-byte bank window,
+  // so a lane's offsets repeat every window along a row: keep one window's
+  // worth (RDC chunk pairs, RDT d tiles) and add the window offset as an
+  // immediate.
+  constexpr int RDC = DC < 8 ? DC : 8;
+  constexpr int RDT = DT < 4 ? DT : 4;
+  u32x4 qf[Q_LDS ? 1 : QB][Q_LDS ? 1 : DC];
+  int q_rd[Q_LDS ? RDC : 1];
+  if constexpr (Q_LDS) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int dc = 0; dc < RDC; ++dc)
+      q_rd[dc] = ((wave * 32 + m) * D + (((2 * dc + h) ^ swz_dual<D>(m)) * 8)) * 2;
+    // direct loads of the Q tile: slot p = i*256 + tid is tile row p / CPR at
+    // chunk position p % CPR (global chunk (p % CPR) ^ swz(row))
+    constexpr int QLOADS = BQ * CPR / kThreads;
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      qf[qb][dc] = bload16(rq, (uint32_t)(((qw0 + qb * 32 + m) * D + dc * 16 + 8 * h) * 2), 0);
+    for (int i = 0; i < QLOADS; ++i) {
+      const int p = i * kThreads + tid;
+      const int row = p / CPR, cpos = p % CPR;
+      bload16_lds(rq, (char*)sQ + (i * kThreads + wave * 64) * 16,
+                  (uint32_t)(row * ROWB + ((cpos ^ swz_dual<D>(row)) * 16)),
+                  (uint32_t)(qt * BQ * ROWB));
+    }
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        qf[qb][dc] = bload16(rq, (uint32_t)(((qw0 + qb * 32 + m) * D + dc * 16 + 8 * h) * 2), 0);
+  }
 
   // K operand (A of S^T): row kt*32 + perm_k(m), chunk 2dc+h, swizzled.
-  int k_rd[DC];
+  int k_rd[RDC];
   {
     const int row = perm_k(m);
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) k_rd[dc] = (row * D + (((2 * dc + h) ^ swz_dual<D>(row)) * 8)) * 2;
+    for (int dc = 0; dc < RDC; ++dc) k_rd[dc] = (row * D + (((2 * dc + h) ^ swz_dual<D>(row)) * 8)) * 2;
   }
+  auto k_off = [&](int dc) { return k_rd[dc % RDC] + (dc / RDC) * 256; };
+  auto q_off = [&](int dc) { return q_rd[dc % RDC] + (dc / RDC) * 256; };
   // V^T operand (A of O^T) through the transposing read.  In 16-lane group g
   // (gg = g % 2), lane i = 4j + q reads key 8h + 4r + j (r: which half of the
   // 8 k-slots) at the 4-element d quad dquad(gg, q) = 16(q%2) + 8gg + 4(q/2)
   // of d tile dt; lane i then receives d = perm_o(16gg + i) for 4 keys.
-  int v_tr[DT];
+  int v_tr[RDT];
   {
     const int i = lane & 15, gg = (lane >> 4) & 1;
     const int j = i >> 2, q = i & 3;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < RDT; ++dt) {
       const int chunk = 4 * dt + 2 * (q & 1) + gg;
       v_tr[dt] = (8 * h + j) * ROWB + ((chunk ^ swz_tr<D>(j)) * 16) + (q >> 1) * 8;
     }
   }
+  auto v_off = [&](int dt) { return v_tr[dt % RDT] + (dt / RDT) * 256; };
   // Direct-load slots: thread slot p = i*256 + tid holds tile row p / CPR at
   // swizzled chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
   uint32_t k_gl[LOADS], v_gl[LOADS];
@@ -274,10 +332,21 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 af = *(const u32x4*)(Kb + kt * 32 * ROWB + k_rd[dc]);
+        const u32x4 af = *(const u32x4*)(Kb + kt * 32 * ROWB + k_off(dc));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
+          if constexpr (Q_LDS) {
+            const u32x4 bq = *(const u32x4*)((const char*)sQ + q_off(dc));
+            sc.v[qb][kt] = mfma32<BF16>(af, bq, sc.v[qb][kt]);
+            // Keep each MFMA next to its two operand reads: left free, the
+            // scheduler hoists all of a tile's reads (128 registers) ahead
+            // of the chain, since with one wave per SIMD it counts the
+            // accumulation registers as headroom.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          } else {
+            sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
+          }
         }
       }
     return sc;
@@ -320,11 +389,15 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x2 lo = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB);
-          const u32x2 hi = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB + 4 * ROWB);
+          const u32x2 lo = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB);
+          const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB + 4 * ROWB);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
+          if constexpr (Q_LDS) {  // as in compute_scores
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          }
         }
     };
     if constexpr (!BF16) {
@@ -427,6 +500,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
           big = big || (__ballot(need[qb]) != 0ull);
         }
 #if FA_FWD_SCHED_VALU > 0
+        if constexpr (!Q_LDS) {
         // Interleave the next tile's score MFMAs with this tile's VALU work:
         // operand reads first, then one MFMA per group of VALU instructions.
         __builtin_amdgcn_sched_group_barrier(0x100, DC * KT, 0);
@@ -434,6 +508,7 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
         for (int i = 0; i < QB * KT * DC; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, FA_FWD_SCHED_VALU, 0);
+        }
         }
 #endif
         if (big) {
@@ -527,11 +602,15 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x2 lo = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB);
-          const u32x2 hi = lds_read_tr16(Vb + v_tr[dt] + kc * 16 * ROWB + 4 * ROWB);
+          const u32x2 lo = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB);
+          const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB + 4 * ROWB);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
+          if constexpr (Q_LDS) {  // as in compute_scores
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+          }
         }
     };
     if (any_grow) {
@@ -542,17 +621,19 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
   };
 
   // Software pipeline over K/V tiles, kStages LDS stages deep.  Iteration j
-  // (tile j in stage j % kStages) starts the loads of tile j + kStages - 1,
-  // issues the score MFMAs of tile j + 1 - independent of this tile's softmax,
-  // so the matrix cores have work while the softmax runs on the VALU - then
-  // runs the softmax and P V of tile j.  Before the group barrier it waits
-  // until tile j + 2 has landed (needed by the next iteration's scores).
-  // Direct loads complete in issue order, so this is "all but the newest k".
+  // (tile j in stage j % kStages) starts the loads of tile j + kStages - 1
+  // (into the stage tile j - 1 left), issues the score MFMAs of tile j + 1 -
+  // independent of this tile's softmax, so the matrix cores have work while
+  // the softmax runs on the VALU - then runs the softmax and P V of tile j.
+  // Before the group barrier it waits until tile j + 2 has landed (needed by
+  // the next iteration's scores).  Direct loads complete in issue order, so
+  // this is "all but the newest kStages - 3 tiles".
   constexpr int kTileLoads = 2 * LOADS;  // direct loads per thread per tile
-  static_assert(kStages == 4, "the pipeline below assumes four stages");
+  constexpr int kAhead = kStages - 1;    // prefetch distance in tiles
   auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
     constexpr int st = decltype(stage_tag)::value;
-    if (j + 3 < n_kt) issue_tile(j + 3, sK[(st + 3) % kStages], sV[(st + 3) % kStages]);
+    if (j + kAhead < n_kt)
+      issue_tile(j + kAhead, sK[(st + kAhead) % kStages], sV[(st + kAhead) % kStages]);
     // On the last tile this reads a stale (in-bounds) stage whose scores are
     // never used; keeping it unconditional keeps it in one basic block with
     // the exponentials.
@@ -569,30 +650,35 @@ __global__ __launch_bounds__(kThreads, FA_FWD_MIN_WAVES) void fwd_kernel(FwdArgs
     } else {
       issue_next();
     }
-    if (j + 3 < n_kt) {
-      wait_vmem_keep<kTileLoads>();
+    if (j + kAhead < n_kt) {
+      wait_vmem_keep<(kStages - 3) * kTileLoads>();
     } else {
       wait_vmem();
     }
     __syncthreads();
   };
 
+  // (with Q_LDS the Q tile's loads were issued first, so they land first)
 #pragma unroll
-  for (int s0 = 0; s0 < 3; ++s0)
+  for (int s0 = 0; s0 < kAhead; ++s0)
     if (s0 < n_kt) issue_tile(s0, sK[s0], sV[s0]);
-  if (2 < n_kt) {
-    wait_vmem_keep<kTileLoads>();  // tiles 0 and 1 have landed
+  if (kAhead < n_kt) {
+    wait_vmem_keep<(kStages - 3) * kTileLoads>();  // tiles 0 and 1 have landed
   } else {
     wait_vmem();
   }
   __syncthreads();
   Scores sa = compute_scores(sK[0], j0 * BK);
   Scores sb;
-  for (int j = 0; j < n_kt; j += 4) {
+  for (int j = 0; j < n_kt; j += kStages) {
     iteration(j, std::integral_constant<int, 0>{}, sa, sb);
     if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
     if (j + 2 < n_kt) iteration(j + 2, std::integral_constant<int, 2>{}, sa, sb);
-    if (j + 3 < n_kt) iteration(j + 3, std::integral_constant<int, 3>{}, sb, sa);
+    if constexpr (kStages == 4) {
+      if (j + 3 < n_kt) iteration(j + 3, std::integral_constant<int, 3>{}, sb, sa);
+    } else {
+      sa = sb;  // an odd number of tiles per round: the next round starts from sb
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
@@ -750,6 +836,7 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
   const bool bias = p.bias != nullptr;
   if (p.d == 64) return bias ? launch_fwd_d<64, false, true>(p, s) : launch_fwd_d<64, false, false>(p, s);
   if (p.d == 128) return bias ? launch_fwd_d<128, false, true>(p, s) : launch_fwd_d<128, false, false>(p, s);
+  if (p.d == 256) return bias ? launch_fwd_d<256, false, true>(p, s) : launch_fwd_d<256, false, false>(p, s);
   return hipErrorInvalidValue;
 }
 
@@ -757,10 +844,15 @@ hipError_t launch_fwd_splitkv(const FwdProblem& p, hipStream_t s) {
   if (p.bias != nullptr) return hipErrorInvalidValue;
   if (p.d == 64) return launch_fwd_d<64, true, false>(p, s);
   if (p.d == 128) return launch_fwd_d<128, true, false>(p, s);
+  if (p.d == 256) return launch_fwd_d<256, true, false>(p, s);
   return hipErrorInvalidValue;
 }
 
-int fwd_key_tile(int d) { return d == 64 ? FwdCfg<64>::BK : FwdCfg<128>::BK; }
-int fwd_query_tile(int d) { return kWaves * (d == 64 ? FwdCfg<64>::QB : FwdCfg<128>::QB) * 32; }
+int fwd_key_tile(int d) {
+  return d == 64 ? FwdCfg<64>::BK : d == 128 ? FwdCfg<128>::BK : FwdCfg<256>::BK;
+}
+int fwd_query_tile(int d) {
+  return kWaves * (d == 64 ? FwdCfg<64>::QB : d == 128 ? FwdCfg<128>::QB : FwdCfg<256>::QB) * 32;
+}
 
 }  // namespace fa

@@ -11,9 +11,13 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+// Head dimensions: the forward covers 64, 128 and 256; the backward 64 and 128.
+bool fwd_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool bwd_head_dim(int d) { return d == 64 || d == 128; }
+
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype, bool fwd) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(fwd ? fwd_head_dim(d) : bwd_head_dim(d))) return FA_ERR_HEADDIM;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
   if (dtype < FA_F16 || dtype > FA_BF16_OUT_F32) return FA_ERR_DTYPE;
@@ -29,7 +33,7 @@ extern "C" {
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int N, int d, float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, true);
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_ALIGN;
@@ -53,7 +57,7 @@ int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void*
                         int B, int H, int N, int d, float scale, int causal, int dtype,
                         void* stream) {
   if (!q || !k || !v || !bias || !o || !lse) return FA_ERR_NULL;
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, true);
   if (st != FA_OK) return st;
   if (N > 46340) return FA_ERR_SHAPE;  // one head's N x N bias must span < 2^32 bytes
   if (bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
@@ -81,14 +85,14 @@ int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void*
 }
 
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  if (B < 1 || H < 1 || N < 1 || !fwd_head_dim(d)) return 0;
   if (num_splits < 1 || num_splits > 64) return 0;
   return (size_t)num_splits * B * H * N * (d + 1) * sizeof(float);
 }
 
 int flash_attn_fwd_splitkv_default_splits(int B, int H, int N, int d, int causal) {
   (void)causal;
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 1;
+  if (B < 1 || H < 1 || N < 1 || !fwd_head_dim(d)) return 1;
   // Splitting costs a float32 partial O per split and a merge pass, so it pays
   // only when the unsplit grid leaves compute units idle (at most one
   // workgroup per CU, 256 CUs) over long key ranges: then aim for two
@@ -108,7 +112,7 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                            float scale, int causal, int dtype, int num_splits, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, true);
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > 64) return FA_ERR_SPLITS;
   if ((long long)num_splits * B * H * N * (d + 1) >= (1LL << 31)) return FA_ERR_SHAPE;
@@ -145,7 +149,7 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                    int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, false);
   if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
@@ -179,7 +183,7 @@ int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                         float scale, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, false);
   if (st != FA_OK) return st;
   if (N > 46340 || bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
@@ -217,7 +221,7 @@ int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void*
 // for a stage are left NULL).
 static int bwd_stage_setup(fa::BwdProblem& p, const void* workspace, size_t workspace_bytes, int B,
                            int H, int N, int d, float scale, int causal, int dtype) {
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+  int st = check_common(B, H, N, d, scale, causal, dtype, false);
   if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
@@ -290,7 +294,7 @@ const char* flash_attn_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, causal 0/1)";
-    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (forward) or 64 or 128 (backward)";
     case FA_ERR_DTYPE: return "unknown dtype code";
     case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -301,6 +305,6 @@ const char* flash_attn_status_string(int status) {
   }
 }
 
-int flash_attn_version(void) { return 101; }
+int flash_attn_version(void) { return 102; }
 
 }  // extern "C"

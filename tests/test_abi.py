@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.flash_attn_version() >= 101
+    assert lib.flash_attn_version() >= 102
     assert lib.status_string(0) == "ok"
     for st in range(1, 10):
         assert lib.status_string(st) not in ("ok", "unknown status")
@@ -79,7 +79,7 @@ def bwd(lib, **kw):
     (dict(q=None), 1), (dict(lse=None), 1), (dict(o=None), 1),
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(N=1 << 30), 2),
     (dict(causal=2), 2),
-    (dict(d=32), 3), (dict(d=256), 3), (dict(d=96), 3),
+    (dict(d=32), 3), (dict(d=512), 3), (dict(d=96), 3), (dict(d=192), 3),
     (dict(dtype=4), 4), (dict(dtype=-1), 4),
     (dict(v=P + 2), 5), (dict(lse=P + 4), 5),
     (dict(scale=0.0), 8), (dict(scale=float("inf")), 8), (dict(scale=float("nan")), 8),
@@ -90,7 +90,7 @@ def test_fwd_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dout=None), 1), (dict(dv=None), 1),
-    (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=7), 4),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(d=256), 3), (dict(dtype=7), 4),
     (dict(dq=P + 8), 5), (dict(workspace=P + 8), 5),
     (dict(workspace=None), 7), (dict(workspace_bytes=8 * 8 - 1), 7),
     (dict(scale=-1.0), 8),
@@ -123,7 +123,8 @@ def test_product_path_has_no_oracle_or_allocation():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), 1), (dict(workspace=None), 7), (dict(workspace_bytes=10), 7),
-    (dict(d=100), 3), (dict(dtype=9), 4), (dict(o=P + 4), 5), (dict(workspace=P + 4), 5),
+    (dict(d=100), 3), (dict(d=256), 3), (dict(dtype=9), 4), (dict(o=P + 4), 5),
+    (dict(workspace=P + 4), 5),
 ])
 def test_bwd_preprocess_validation(lib, kw, status):
     args = dict(o=P, lse=P, dout=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1, N=8, d=64,
@@ -134,7 +135,7 @@ def test_bwd_preprocess_validation(lib, kw, status):
 
 @pytest.mark.parametrize("stage", ["dkdv", "dq"])
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(workspace=None), 7), (dict(N=0), 2), (dict(d=16), 3),
+    (dict(q=None), 1), (dict(workspace=None), 7), (dict(N=0), 2), (dict(d=16), 3), (dict(d=256), 3),
     (dict(scale=0.0), 8), (dict(causal=3), 2), (dict(k=P + 2), 5),
 ])
 def test_bwd_stage_validation(lib, stage, kw, status):
@@ -153,7 +154,8 @@ def test_bwd_stage_validation(lib, stage, kw, status):
 def test_splitkv_workspace_and_default_splits(lib):
     assert lib.flash_attn_fwd_splitkv_workspace_bytes(2, 12, 1024, 64, 3) == 4 * 3 * 24 * 1024 * 65
     assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 8, 128, 1) == 4 * 8 * 129
-    for bad in (dict(num_splits=0), dict(num_splits=65), dict(d=96), dict(N=0)):
+    assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 2, 100, 256, 2) == 4 * 2 * 2 * 100 * 257
+    for bad in (dict(num_splits=0), dict(num_splits=65), dict(d=96), dict(d=512), dict(N=0)):
         args = dict(B=1, H=1, N=8, d=64, num_splits=2)
         args.update(bad)
         assert lib.flash_attn_fwd_splitkv_workspace_bytes(**args) == 0
@@ -165,6 +167,9 @@ def test_splitkv_workspace_and_default_splits(lib):
     assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 8192, 64, 0) == 4
     assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 16384, 64, 1) == 4
     assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 64, 64, 0) == 1
+    # d=256 tiles are 128 queries x 32 keys: 16 workgroups at N=2048, 64 key tiles
+    assert lib.flash_attn_fwd_splitkv_default_splits(1, 1, 2048, 256, 0) == 2
+    assert lib.flash_attn_fwd_splitkv_default_splits(2, 8, 4096, 256, 0) == 1
     for B, H, N, d, c in ((1, 1, 1, 64, 0), (4, 4, 300, 128, 1), (1, 8, 32768, 64, 1)):
         assert 1 <= lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, c) <= 16
 
@@ -184,6 +189,7 @@ def test_fwd_splitkv_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bias=None), 1), (dict(q=None), 1), (dict(N=0), 2), (dict(N=46344), 2), (dict(d=32), 3),
+    (dict(d=512), 3),
     (dict(dtype=6), 4), (dict(bias=P + 2), 5), (dict(N=12), 5), (dict(bias_stride_b=4), 5),
     (dict(bias_stride_h=12), 5), (dict(bias_stride_b=-8), 2), (dict(scale=0.0), 8),
 ])
@@ -196,7 +202,7 @@ def test_fwd_bias_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bias=None), 1), (dict(dv=None), 1), (dict(N=0), 2), (dict(N=46344), 2),
-    (dict(bias_stride_h=-8), 2), (dict(d=48), 3), (dict(dtype=9), 4), (dict(bias=P + 8), 5),
+    (dict(bias_stride_h=-8), 2), (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=9), 4), (dict(bias=P + 8), 5),
     (dict(N=20), 5), (dict(bias_stride_b=12), 5), (dict(workspace=None), 7),
     (dict(workspace_bytes=8 * 8 - 1), 7), (dict(scale=float("inf")), 8),
 ])

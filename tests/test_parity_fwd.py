@@ -63,10 +63,10 @@ def test_tiny_fwd_workload():
 @pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, False),
                                          (si.FMT_F16, True), (si.FMT_BF16, True)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 2, 17, 64, 100, 129, 256, 300, 520])
 def test_small_shapes(N, d, causal, fmt, out_f32):
-    """Tails, single tiles, several tiles, both head dims, masks and dtypes."""
+    """Tails, single tiles, several tiles, every head dim, masks and dtypes."""
     w = si.random_case(1, 2, N, d, fmt, causal, seed=N + d)
     o, lse = run_fwd(w, out_f32=out_f32)
     check(w, o, lse)
@@ -174,6 +174,23 @@ def test_deterministic_and_in_bounds():
     check(w, o, lse)
 
 
+@pytest.mark.parametrize("fmt,out_f32,causal", [(si.FMT_F16, False, False), (si.FMT_BF16, True, True)])
+def test_head_dim_256_full(fmt, out_f32, causal):
+    """d=256 (LDS-resident Q, three K/V stages) at B=1 H=4 N=1000: 32 key
+    tiles and a ragged tail, every element."""
+    w = si.random_case(1, 4, 1000, 256, fmt, causal, seed=256)
+    o, lse = run_fwd(w, out_f32=out_f32)
+    check(w, o, lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_sampled(causal):
+    """d=256 at B=2 H=8 N=4096 bf16 (float32 O), on sampled rows."""
+    w = si.random_case(2, 8, 4096, 256, si.FMT_BF16, causal, seed=257)
+    o, lse = run_fwd(w, out_f32=True)
+    check(w, o, lse, rows=sample_rows(w, 192, 257))
+
+
 def test_errors_through_binding():
     import torch
     import io_aware_exact_08_amd as fa
@@ -206,7 +223,7 @@ def run_splitkv(w, num_splits, out_f32=False):
 
 @pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, True)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N,splits", [(1, 1), (1, 3), (37, 2), (64, 5), (200, 2), (200, 3),
                                       (520, 4), (520, 64), (1000, 7)])
 def test_splitkv_small_shapes(N, splits, d, causal, fmt, out_f32):
@@ -283,7 +300,7 @@ def check_bias(w, bias_bits, o, lse, tag=""):
 
 @pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, True)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [8, 64, 200, 520])
 @pytest.mark.parametrize("layout", ["shared", "per_head", "per_batch_head"])
 def test_bias_random(N, d, causal, fmt, out_f32, layout):
