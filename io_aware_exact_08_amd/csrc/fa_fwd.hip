@@ -67,6 +67,9 @@ namespace fa {
 #ifndef FA_FWD_MIN_WAVES
 #define FA_FWD_MIN_WAVES 2
 #endif
+#ifndef FA_FWD256_PREFETCH
+#define FA_FWD256_PREFETCH 0
+#endif
 
 template <int D>
 struct FwdCfg;
@@ -76,6 +79,7 @@ struct FwdCfg<64> {
   static constexpr int BK = FA_FWD64_BK;  // keys per tile
   static constexpr int STAGES = FA_FWD_STAGES;        // K/V tiles resident in LDS
   static constexpr bool Q_LDS = false;                // Q^T operand from LDS (else registers)
+  static constexpr bool PREFETCH = true;              // next tile's scores during this softmax
   static constexpr int MIN_WAVES = FA_FWD_MIN_WAVES;  // waves per SIMD the registers allow
 };
 template <>
@@ -84,6 +88,7 @@ struct FwdCfg<128> {
   static constexpr int BK = 32;
   static constexpr int STAGES = FA_FWD_STAGES;
   static constexpr bool Q_LDS = false;
+  static constexpr bool PREFETCH = true;
   static constexpr int MIN_WAVES = FA_FWD_MIN_WAVES;
 };
 // d=256: the O^T accumulators alone take 128 registers per lane, so the Q^T
@@ -99,6 +104,7 @@ struct FwdCfg<256> {
   static constexpr int BK = 32;
   static constexpr int STAGES = 3;
   static constexpr bool Q_LDS = true;
+  static constexpr bool PREFETCH = FA_FWD256_PREFETCH;
   static constexpr int MIN_WAVES = 1;
 };
 
@@ -113,6 +119,33 @@ constexpr float rescale_threshold() { return BF16 ? 0.0f : 8.0f; }
 // fp16 fast path: largest row sum of rounded probabilities per tile that
 // keeps the current reference.
 constexpr float kLazyBound = 4096.0f;
+
+#ifndef FA_QLDS_LOOKAHEAD
+#define FA_QLDS_LOOKAHEAD 4
+#endif
+// Operand-read placement for a chain of MFMAs that each take two LDS reads
+// (LDS-resident Q path): the reads of the first LA MFMAs go first, then each
+// MFMA is followed by the reads of the one LA places later.  Left free, the
+// scheduler hoists all of a tile's reads (128 registers) ahead of the chain,
+// since with one wave per SIMD it counts the accumulation registers as
+// headroom.  A scheduling group fills from the instructions before its
+// barrier, so pin_step(i) follows the code of MFMA i and pin_tail the chain.
+template <int sync>
+__device__ __forceinline__ void pin_step(int i) {
+  constexpr int LA = FA_QLDS_LOOKAHEAD;
+  if (i == LA - 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, sync);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+  } else if (i >= LA) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, sync);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+  }
+}
+template <int sync>
+__device__ __forceinline__ void pin_tail() {
+#pragma unroll
+  for (int i = 1; i < FA_QLDS_LOOKAHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+}
 
 struct FwdArgs {
   const uint16_t* q;
@@ -338,17 +371,13 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           if constexpr (Q_LDS) {
             const u32x4 bq = *(const u32x4*)((const char*)sQ + q_off(dc));
             sc.v[qb][kt] = mfma32<BF16>(af, bq, sc.v[qb][kt]);
-            // Keep each MFMA next to its two operand reads: left free, the
-            // scheduler hoists all of a tile's reads (128 registers) ahead
-            // of the chain, since with one wave per SIMD it counts the
-            // accumulation registers as headroom.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            pin_step<1>(kt * DC + dc);
           } else {
             sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
           }
         }
       }
+    if constexpr (Q_LDS) pin_tail<1>();
     return sc;
   };
 
@@ -394,11 +423,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
-          if constexpr (Q_LDS) {  // as in compute_scores
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-          }
+          if constexpr (Q_LDS) pin_step<2>(dt * KC + kc);
         }
+      if constexpr (Q_LDS) pin_tail<2>();
     };
     if constexpr (!BF16) {
       // ---- fp16: lazy reference, overflow detected from the rounded sum ----
@@ -554,6 +581,17 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       grow[qb] = mnew[qb] > m_run[qb] + rescale_threshold<BF16>();
       any_grow = any_grow || (__ballot(grow[qb]) != 0ull);
     }
+    // Only rows that grew move their reference (the others get alpha = 1
+    // exactly), so each row depends on its own data alone.
+    auto rescale = [&](int qb) {
+      const float mn = grow[qb] ? mnew[qb] : m_run[qb];
+      const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2(m_run[qb] - mn);
+      m_run[qb] = mn;
+      l_run[qb] *= alpha;
+      if constexpr (BF16) l32_run[qb] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
+    };
     // Exponentiate, round, sum and multiply by V^T.  Instantiated twice so
     // that the path without a rescale carries no merge copies of O.
     auto finish = [&](auto rescale_tag) {
@@ -561,17 +599,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       u32x4 pf[QB][KC];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if constexpr (RESCALE) {
-          // Only rows that grew move their reference (the others get
-          // alpha = 1 exactly), so each row depends on its own data alone.
-          const float mn = grow[qb] ? mnew[qb] : m_run[qb];
-          const float alpha = (m_run[qb] == -INFINITY) ? 0.f : fast_exp2(m_run[qb] - mn);
-          m_run[qb] = mn;
-          l_run[qb] *= alpha;
-          if constexpr (BF16) l32_run[qb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) oacc[qb][dt] *= alpha;
-        }
+        if constexpr (RESCALE) rescale(qb);
         const float neg_m = (m_run[qb] == -INFINITY) ? 0.f : -m_run[qb];
         float ls[4] = {0.f, 0.f, 0.f, 0.f};
         float ls32[2] = {0.f, 0.f};
@@ -607,11 +635,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
-          if constexpr (Q_LDS) {  // as in compute_scores
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-          }
+          if constexpr (Q_LDS) pin_step<2>(dt * KC + kc);
         }
+      if constexpr (Q_LDS) pin_tail<2>();
     };
     if (any_grow) {
       finish(std::true_type{});
@@ -630,6 +656,10 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // this is "all but the newest kStages - 3 tiles".
   constexpr int kTileLoads = 2 * LOADS;  // direct loads per thread per tile
   constexpr int kAhead = kStages - 1;    // prefetch distance in tiles
+  // Without the score prefetch (PREFETCH false) an iteration computes its own
+  // tile's scores first and the next iteration needs only tile j + 1.
+  constexpr bool PREFETCH = FwdCfg<D>::PREFETCH;
+  constexpr int kKeep = (PREFETCH ? kStages - 3 : kStages - 2) * kTileLoads;
   auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
     constexpr int st = decltype(stage_tag)::value;
     if (j + kAhead < n_kt)
@@ -637,10 +667,13 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     // On the last tile this reads a stale (in-bounds) stage whose scores are
     // never used; keeping it unconditional keeps it in one basic block with
     // the exponentials.
-    auto issue_next = [&]() { nxt = compute_scores(sK[(st + 1) % kStages], (j0 + j + 1) * BK); };
+    auto issue_next = [&]() {
+      if constexpr (PREFETCH) nxt = compute_scores(sK[(st + 1) % kStages], (j0 + j + 1) * BK);
+    };
     const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
     if (active) {
+      if constexpr (!PREFETCH) cur = compute_scores(sK[st], k0);
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
       if (need_mask) {
         softmax_pv(std::true_type{}, cur, sV[st], k0, j == 0, issue_next);
@@ -651,7 +684,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       issue_next();
     }
     if (j + kAhead < n_kt) {
-      wait_vmem_keep<(kStages - 3) * kTileLoads>();
+      wait_vmem_keep<kKeep>();
     } else {
       wait_vmem();
     }
@@ -663,20 +696,20 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   for (int s0 = 0; s0 < kAhead; ++s0)
     if (s0 < n_kt) issue_tile(s0, sK[s0], sV[s0]);
   if (kAhead < n_kt) {
-    wait_vmem_keep<(kStages - 3) * kTileLoads>();  // tiles 0 and 1 have landed
+    wait_vmem_keep<kKeep>();  // tiles 0 and 1 (without the prefetch: tile 0) have landed
   } else {
     wait_vmem();
   }
   __syncthreads();
-  Scores sa = compute_scores(sK[0], j0 * BK);
-  Scores sb;
+  Scores sa, sb;
+  if constexpr (PREFETCH) sa = compute_scores(sK[0], j0 * BK);
   for (int j = 0; j < n_kt; j += kStages) {
     iteration(j, std::integral_constant<int, 0>{}, sa, sb);
     if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{}, sb, sa);
     if (j + 2 < n_kt) iteration(j + 2, std::integral_constant<int, 2>{}, sa, sb);
     if constexpr (kStages == 4) {
       if (j + 3 < n_kt) iteration(j + 3, std::integral_constant<int, 3>{}, sb, sa);
-    } else {
+    } else if constexpr (PREFETCH) {
       sa = sb;  // an odd number of tiles per round: the next round starts from sb
     }
   }
