@@ -138,8 +138,14 @@ def config_sweep(fa, si, torch, np, dev):
         return conv(w.q), conv(w.k), conv(w.v), (conv(w.do) if w.do is not None else None)
 
     def timed(fn, reps):
-        for _ in range(3):
+        # the clocks need about 0.2 s of sustained load to settle
+        t0 = time.perf_counter()
+        n = 0
+        while n < 3 or time.perf_counter() - t0 < 0.25:
             fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -160,7 +166,8 @@ def config_sweep(fa, si, torch, np, dev):
             ms = timed(lambda: fa.flash_attn_fwd_bias(q, k, v, bias, causal=w.causal, scale=w.scale,
                                                       out_f32=out_f32, o=o, lse=lse), reps)
             rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal, "bias": list(bias.shape),
-                   "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+                   "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                   "fwd_frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
             if bwd:
                 ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32,
                                  device=dev)
@@ -170,6 +177,8 @@ def config_sweep(fa, si, torch, np, dev):
                                                             dk=dk, dv=dv, workspace=ws), reps)
                 rec["bwd_ms"] = round(ms_b, 4)
                 rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
+                # executed work: dK/dV 8 and dQ 6 BHN^2d products = 3.5x the forward's
+                rec["bwd_frac_of_peak"] = round(3.5 * fl / (ms_b * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)
             out[name] = rec
             return
         if splits is None:
@@ -184,7 +193,8 @@ def config_sweep(fa, si, torch, np, dev):
                                                          out_f32=out_f32, num_splits=splits,
                                                          o=o, lse=lse, workspace=ws), reps)
         rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal,
-               "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+               "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+               "fwd_frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
         if splits is not None:
             rec["splits"] = splits
         if bwd:
@@ -196,6 +206,7 @@ def config_sweep(fa, si, torch, np, dev):
                                                    workspace=ws), reps)
             rec["bwd_ms"] = round(ms_b, 4)
             rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
+            rec["bwd_frac_of_peak"] = round(3.5 * fl / (ms_b * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)
         out[name] = rec
 
     for n in (1024, 2048, 4096, 8192):
