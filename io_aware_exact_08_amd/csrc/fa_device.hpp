@@ -184,4 +184,28 @@ __device__ __forceinline__ int swz_tr(int r) {
     return ((r & 1) << 2) | (((r >> 1) & 1) << 3);
 }
 
+// Operand-read placement for a chain of MFMAs that each take R LDS reads:
+// the reads of the first LA MFMAs go first, then each MFMA is followed by the
+// reads of the one LA places later.  Left free, the scheduler can hoist every
+// read of a chain ahead of it (for the d=256 forward with one wave per SIMD,
+// 128 registers, since it counts the accumulation registers as headroom).
+// A scheduling group fills from the instructions before its barrier, so
+// pin_step(i) follows the code of MFMA i (i counted from 0 along the chain)
+// and pin_tail the chain; `sync` separates chains in one scheduling region.
+template <int sync, int R, int LA>
+__device__ __forceinline__ void pin_step(int i) {
+  if (i == LA - 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * LA, sync);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+  } else if (i >= LA) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R, sync);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+  }
+}
+template <int sync, int LA>
+__device__ __forceinline__ void pin_tail() {
+#pragma unroll
+  for (int i = 1; i < LA; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
+}
+
 }  // namespace fa

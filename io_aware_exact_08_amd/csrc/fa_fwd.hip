@@ -123,30 +123,6 @@ constexpr float kLazyBound = 4096.0f;
 #ifndef FA_QLDS_LOOKAHEAD
 #define FA_QLDS_LOOKAHEAD 4
 #endif
-// Operand-read placement for a chain of MFMAs that each take two LDS reads
-// (LDS-resident Q path): the reads of the first LA MFMAs go first, then each
-// MFMA is followed by the reads of the one LA places later.  Left free, the
-// scheduler hoists all of a tile's reads (128 registers) ahead of the chain,
-// since with one wave per SIMD it counts the accumulation registers as
-// headroom.  A scheduling group fills from the instructions before its
-// barrier, so pin_step(i) follows the code of MFMA i and pin_tail the chain.
-template <int sync>
-__device__ __forceinline__ void pin_step(int i) {
-  constexpr int LA = FA_QLDS_LOOKAHEAD;
-  if (i == LA - 1) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, sync);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
-  } else if (i >= LA) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, sync);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
-  }
-}
-template <int sync>
-__device__ __forceinline__ void pin_tail() {
-#pragma unroll
-  for (int i = 1; i < FA_QLDS_LOOKAHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, sync);
-}
-
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -371,13 +347,13 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           if constexpr (Q_LDS) {
             const u32x4 bq = *(const u32x4*)((const char*)sQ + q_off(dc));
             sc.v[qb][kt] = mfma32<BF16>(af, bq, sc.v[qb][kt]);
-            pin_step<1>(kt * DC + dc);
+            pin_step<1, 2, FA_QLDS_LOOKAHEAD>(kt * DC + dc);
           } else {
             sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
           }
         }
       }
-    if constexpr (Q_LDS) pin_tail<1>();
+    if constexpr (Q_LDS) pin_tail<1, FA_QLDS_LOOKAHEAD>();
     return sc;
   };
 
@@ -423,9 +399,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
-          if constexpr (Q_LDS) pin_step<2>(dt * KC + kc);
+          if constexpr (Q_LDS) pin_step<2, 2, FA_QLDS_LOOKAHEAD>(dt * KC + kc);
         }
-      if constexpr (Q_LDS) pin_tail<2>();
+      if constexpr (Q_LDS) pin_tail<2, FA_QLDS_LOOKAHEAD>();
     };
     if constexpr (!BF16) {
       // ---- fp16: lazy reference, overflow detected from the rounded sum ----
@@ -635,9 +611,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
-          if constexpr (Q_LDS) pin_step<2>(dt * KC + kc);
+          if constexpr (Q_LDS) pin_step<2, 2, FA_QLDS_LOOKAHEAD>(dt * KC + kc);
         }
-      if constexpr (Q_LDS) pin_tail<2>();
+      if constexpr (Q_LDS) pin_tail<2, FA_QLDS_LOOKAHEAD>();
     };
     if (any_grow) {
       finish(std::true_type{});
