@@ -128,8 +128,9 @@ int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void*
  * in order on one stream).  dK/dV and dQ only read the workspace the
  * preprocess wrote, so once it has run they may run on different streams.
  *
- * flash_attn_bwd_preprocess: D_i = sum_c dO_ic O_ic and LSE_i*log2(e) into the
- *   workspace (page 2, "Re-computation": the per-row terms the recompute needs).
+ * flash_attn_bwd_preprocess: -D_i (D_i = sum_c dO_ic O_ic, stored negated) and
+ *   LSE_i*log2(e) into the workspace (page 2, "Re-computation": the per-row
+ *   terms the recompute needs).
  *   `dtype` selects the input type and O's type as for the forward.
  * flash_attn_bwd_dkdv: dK and dV.  Each workgroup keeps a K/V tile and loops
  *   over query tiles, the loop order of that section.

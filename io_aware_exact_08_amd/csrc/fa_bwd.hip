@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __rest
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w, 64);
   if (row < rows && c == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;  // stored negated: it seeds the dP - D accumulators as is
     // a row whose every key is hidden (LSE = -inf, O = 0) must recompute P = 0
     lse2[row] = lse[row] == -INFINITY ? INFINITY : lse[row] * kLog2e;
   }
@@ -88,7 +88,7 @@ struct BwdArgs {
   const uint16_t* v;
   const uint16_t* dout;
   const float* lse2;   // LSE * log2(e)
-  const float* delta;  // D
+  const float* delta;  // -D
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -304,8 +304,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
         const f32x4 d1 = *(const f32x4*)(&sD[qb + 4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dp[t][8 * g + e] = -d0[e];
-          dp[t][8 * g + 4 + e] = -d1[e];
+          dp[t][8 * g + e] = d0[e];
+          dp[t][8 * g + 4 + e] = d1[e];
         }
       }
 #pragma unroll
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   }
   // Rows past N: LSE2 and D read as 0; their Q and dO rows are 0 and dQ is
   // not stored.
-  float lse2, dl;
+  float lse2, dl;  // LSE * log2(e) and -D of this lane's query row
   {
     const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
     const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[kt][r] = -dl;
+      for (int r = 0; r < 16; ++r) dp[kt][r] = dl;  // -D
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const u32x4 ka = *(const u32x4*)(sK + kt * 32 * ROWB + to.rd[dc]);

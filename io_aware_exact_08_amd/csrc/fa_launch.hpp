@@ -38,7 +38,7 @@ struct BwdProblem {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [BH*N] workspace: D
+  float* delta;  // [BH*N] workspace: -D
   float* lse2;   // [BH*N] workspace: LSE * log2(e)
   int BH;
   int N;
