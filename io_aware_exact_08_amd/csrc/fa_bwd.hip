@@ -161,6 +161,14 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 #ifndef FA_BWD_PIN_LA
 #define FA_BWD_PIN_LA 4
 #endif
+// Order of the second product chain (dV/dK, dQ): contraction chunk outermost,
+// so its first half needs only the first 32-row half of P and dS and the
+// second half's exponentials can run under those MFMAs.  Measured on MI355X
+// against d-tile outermost: causal dK/dV -1.7% (B2 H12 N4096 fp16), dQ -1.5%
+// (B1 H8 N32768 bf16 causal) and -0.5% (B2 H12 N8192 fp16), others unchanged.
+#ifndef FA_BWD_CHUNK_MAJOR
+#define FA_BWD_CHUNK_MAJOR 1
+#endif
 
 // ---------------------------------------------------------------------------
 // dK, dV: workgroup owns 128 keys (32 per wave); loop over 64-row query tiles.
@@ -368,16 +376,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       }
     // dV^T += dO^T P ; dK^T += Q^T dS   (rows: d with perm_o, cols: keys)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        const u32x4 ga = tr_operand(sG, to.trl[dt], to.trh[dt], qc, ROWB);
-        const u32x4 qa = tr_operand(sQ, to.trl[dt], to.trh[dt], qc, ROWB);
-        dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
-        pin_step<2, 2, FA_BWD_PIN_LA>(2 * (dt * QC + qc));
-        dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
-        pin_step<2, 2, FA_BWD_PIN_LA>(2 * (dt * QC + qc) + 1);
-      }
+    for (int i = 0; i < DT * QC; ++i) {
+      const int dt = FA_BWD_CHUNK_MAJOR ? i % DT : i / QC;
+      const int qc = FA_BWD_CHUNK_MAJOR ? i / DT : i % QC;
+      const u32x4 ga = tr_operand(sG, to.trl[dt], to.trh[dt], qc, ROWB);
+      const u32x4 qa = tr_operand(sQ, to.trl[dt], to.trh[dt], qc, ROWB);
+      dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
+      pin_step<2, 2, FA_BWD_PIN_LA>(2 * i);
+      dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
+      pin_step<2, 2, FA_BWD_PIN_LA>(2 * i + 1);
+    }
     pin_tail<2, FA_BWD_PIN_LA>();
   };
 
@@ -595,13 +603,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     }
     // dQ^T += K^T dS^T (rows: d with perm_o, cols: queries)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const u32x4 ka = tr_operand(sK, to.trl[dt], to.trh[dt], kc, ROWB);
-        dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
-        pin_step<2, 2, FA_BWD_PIN_LA>(dt * KC + kc);
-      }
+    for (int i = 0; i < DT * KC; ++i) {
+      const int dt = FA_BWD_CHUNK_MAJOR ? i % DT : i / KC;
+      const int kc = FA_BWD_CHUNK_MAJOR ? i / DT : i % KC;
+      const u32x4 ka = tr_operand(sK, to.trl[dt], to.trh[dt], kc, ROWB);
+      dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
+      pin_step<2, 2, FA_BWD_PIN_LA>(i);
+    }
     pin_tail<2, FA_BWD_PIN_LA>();
   };
 
