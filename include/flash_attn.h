@@ -88,7 +88,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * per tile from Q, K and the forward's LSE.  Gradients of L = <dO, O>:
  *   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
  *   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
- * Three kernels on `stream`: D and LSE*log2(e) (one pass over O, dO and LSE),
+ * Three kernels on `stream`: -D and -LSE*log2(e) (one pass over O, dO and LSE),
  * dK/dV (each workgroup keeps a K/V tile and loops over query tiles, the loop
  * order of that section), dQ (each workgroup keeps a query tile and loops
  * over K/V tiles).
@@ -210,7 +210,7 @@ size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int nu
 int flash_attn_fwd_splitkv_default_splits(int B, int H, int N, int d, int causal);
 
 /* Bytes of workspace flash_attn_bwd needs (8 * B * H * N: two floats per row,
- * D and LSE*log2(e)); 0 for invalid sizes. */
+ * -D and -LSE*log2(e)); 0 for invalid sizes. */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Static, NUL-terminated description of a status code. */

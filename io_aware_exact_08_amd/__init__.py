@@ -240,7 +240,7 @@ def _check_ws(workspace, B, H, N, d):
 
 
 def flash_attn_bwd_preprocess(o, lse, dout, workspace, in_dtype=None):
-    """Stage 1 of the backward: D and LSE*log2(e) into `workspace`."""
+    """Stage 1 of the backward: -D and -LSE*log2(e) into `workspace`."""
     torch = _torch()
     B, H, N, d = dout.shape
     in_dtype = dout.dtype if in_dtype is None else in_dtype

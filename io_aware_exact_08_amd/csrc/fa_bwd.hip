@@ -11,7 +11,7 @@
 //   dK = scale dS^T Q,       dQ = scale dS K.
 //
 // Three kernels, all deterministic (no atomics):
-//  * bwd_pre   : D and LSE*log2(e) for every row (one pass over O and dO).
+//  * bwd_pre   : -D and -LSE*log2(e) for every row (one pass over O and dO).
 //  * bwd_dkdv  : a workgroup keeps 128 keys of K and V in registers (32 per
 //                wave) and loops over 64-row Q/dO tiles (the loop order
 //                above); dK and dV accumulate in registers.
@@ -36,7 +36,7 @@ namespace fa {
 constexpr int kBwdThreads = 256;
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic and LSE_i * log2(e)
+// -D_i = -sum_c dO_ic O_ic and -LSE_i * log2(e)
 // ---------------------------------------------------------------------------
 template <int D, bool BF16, bool O_F32>
 __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __restrict__ o,
@@ -76,9 +76,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __rest
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w, 64);
   if (row < rows && c == 0) {
-    delta[row] = -acc;  // stored negated: it seeds the dP - D accumulators as is
-    // a row whose every key is hidden (LSE = -inf, O = 0) must recompute P = 0
-    lse2[row] = lse[row] == -INFINITY ? INFINITY : lse[row] * kLog2e;
+    // Both stored negated: they seed the dP - D and c*s - LSE*log2(e)
+    // accumulators as they are.  A row whose every key is hidden (LSE = -inf,
+    // O = 0) must recompute P = 0: its exponent reference is -inf.
+    delta[row] = -acc;
+    lse2[row] = lse[row] == -INFINITY ? -INFINITY : -(lse[row] * kLog2e);
   }
 }
 
@@ -87,7 +89,7 @@ struct BwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* dout;
-  const float* lse2;   // LSE * log2(e)
+  const float* lse2;   // -LSE * log2(e)
   const float* delta;  // -D
   uint16_t* dq;
   uint16_t* dk;
@@ -166,6 +168,9 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 // second half's exponentials can run under those MFMAs.  Measured on MI355X
 // against d-tile outermost: causal dK/dV -1.7% (B2 H12 N4096 fp16), dQ -1.5%
 // (B1 H8 N32768 bf16 causal) and -0.5% (B2 H12 N8192 fp16), others unchanged.
+#ifndef FA_BWD_PRESCALE
+#define FA_BWD_PRESCALE 1
+#endif
 #ifndef FA_BWD_CHUNK_MAJOR
 #define FA_BWD_CHUNK_MAJOR 1
 #endif
@@ -199,6 +204,11 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   constexpr int STAGE = dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
   constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
+  // K is pre-multiplied by c = scale*log2(e) and the S accumulators start at
+  // -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the exponent
+  // c*s - LSE*log2(e) itself: no multiply-add per score (a bias then adds
+  // bias*log2(e), and a zero bias changes nothing).
+  constexpr bool PRE = FA_BWD_PRESCALE;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -249,6 +259,17 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       const uint32_t off = (uint32_t)((key * D + dc * 16 + 8 * h) * 2);
       kf[dc] = bload16(rk, off, 0);
       vf[dc] = bload16(rv, off, 0);
+    }
+    if constexpr (PRE) {
+      // K * c rounded to the input type once: the S MFMAs then yield c*s
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = kf[dc][e];
+          kf[dc][e] = pack2<BF16>(to_f32<BF16>((uint16_t)(w & 0xffffu)) * a.c,
+                                  to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
+        }
     }
   }
   const TileOffsets<D> to(lane);
@@ -315,6 +336,15 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
           dp[t][8 * g + e] = d0[e];
           dp[t][8 * g + 4 + e] = d1[e];
         }
+        if constexpr (PRE) {
+          const f32x4 l0 = *(const f32x4*)(&sL[qb]);
+          const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[t][8 * g + e] = l0[e];
+            s[t][8 * g + 4 + e] = l1[e];
+          }
+        }
       }
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
@@ -328,8 +358,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     }
     pin_tail<1, FA_BWD_PIN_LA>();
     if constexpr (BIAS) {
-      // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e))
-      const float kb = 1.0f / a.scale;
+      // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e));
+      // with PRE the scores are already in log2 units: s + bias*log2(e)
+      const float kb = PRE ? kLog2e : 1.0f / a.scale;
       const char* sB = stage + BIAS_OFF;
 #pragma unroll
       for (int t = 0; t < QT; ++t)
@@ -352,13 +383,18 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int qb = t * 32 + 16 * g + 8 * h;
-        const f32x4 l0 = *(const f32x4*)(&sL[qb]);
+        const f32x4 l0 = *(const f32x4*)(&sL[qb]);  // -LSE*log2(e) (unused with PRE)
         const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
         float pv[8], dsv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float l2 = e < 4 ? l0[e] : l1[e - 4];
-          float p = fast_exp2(__builtin_fmaf(s[t][8 * g + e], c, -l2));
+          float p;
+          if constexpr (PRE) {
+            p = fast_exp2(s[t][8 * g + e]);
+          } else {
+            const float nl2 = e < 4 ? l0[e] : l1[e - 4];
+            p = fast_exp2(__builtin_fmaf(s[t][8 * g + e], c, nl2));
+          }
           if constexpr (MASK) {
             if (key > q0 + qb + e) p = 0.f;
           }
@@ -458,6 +494,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   static_assert(LOADS * kBwdThreads == BK * CPR, "tile split");
   constexpr int STAGE = dq_stage_bytes<D>();
   constexpr int TILE = BK * ROWB;
+  // Q is pre-multiplied by c and the S accumulators start at -LSE*log2(e)
+  // (this lane's row), as in the dK/dV kernel.
+  constexpr bool PRE = FA_BWD_PRESCALE;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -499,14 +538,25 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
       qf[dc] = bload16(rq, off, 0);
       gf[dc] = bload16(rg, off, 0);
     }
+    if constexpr (PRE) {
+      // Q * c rounded to the input type once: the S MFMAs then yield c*s
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = qf[dc][e];
+          qf[dc][e] = pack2<BF16>(to_f32<BF16>((uint16_t)(w & 0xffffu)) * a.c,
+                                  to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
+        }
+    }
   }
   // Rows past N: LSE2 and D read as 0; their Q and dO rows are 0 and dQ is
   // not stored.
-  float lse2, dl;  // LSE * log2(e) and -D of this lane's query row
+  float nl2, dl;  // -LSE * log2(e) and -D of this lane's query row
   {
     const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
     const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
-    lse2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
+    nl2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
     dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
   }
   const TileOffsets<D> to(lane);
@@ -553,7 +603,10 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     for (int kt = 0; kt < KT; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[kt][r] = dl;  // -D
+      for (int r = 0; r < 16; ++r) {
+        dp[kt][r] = dl;  // -D
+        if constexpr (PRE) s[kt][r] = nl2;
+      }
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         const u32x4 ka = *(const u32x4*)(sK + kt * 32 * ROWB + to.rd[dc]);
@@ -566,7 +619,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     }
     pin_tail<1, FA_BWD_PIN_LA>();
     if constexpr (BIAS) {
-      const float kb = 1.0f / a.scale;
+      const float kb = PRE ? kLog2e : 1.0f / a.scale;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -584,7 +637,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
       float dsv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[kt][r], c, -lse2));
+        float p = PRE ? fast_exp2(s[kt][r]) : fast_exp2(__builtin_fmaf(s[kt][r], c, nl2));
         if constexpr (MASK) {
           // causal diagonal; with a bias also keys past N, whose bias entries
           // are read from the next row and must not reach dS

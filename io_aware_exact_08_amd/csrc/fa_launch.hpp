@@ -39,7 +39,7 @@ struct BwdProblem {
   void* dk;
   void* dv;
   float* delta;  // [BH*N] workspace: -D
-  float* lse2;   // [BH*N] workspace: LSE * log2(e)
+  float* lse2;   // [BH*N] workspace: -LSE * log2(e)
   int BH;
   int N;
   int d;
