@@ -160,8 +160,12 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 // and spilled 16.  Measured on MI355X, lookahead 4 against none: causal
 // dK/dV -23% (N=4096) and -20% (N=32768), non-causal dK/dV -1%, dQ -1.5%
 // (non-causal) to -7% (causal N=4096); lookahead 2, 6 and 8 were slower.
+// With the log2-unit scores (fewer VALU instructions per tile) lookahead 3
+// beat 4 on every backward shape measured: dK/dV -0.8% (B2 H12 N8192 fp16),
+// -2.4% (causal N=4096), -0.9% (B1 H8 N32768 bf16 causal), dQ -0.4 to -1.1%;
+// 5 and 6 were not faster than 4.
 #ifndef FA_BWD_PIN_LA
-#define FA_BWD_PIN_LA 4
+#define FA_BWD_PIN_LA 3
 #endif
 // Order of the second product chain (dV/dK, dQ): contraction chunk outermost,
 // so its first half needs only the first 32-row half of P and dS and the
