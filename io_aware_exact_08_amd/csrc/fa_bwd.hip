@@ -208,11 +208,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   constexpr int STAGE = dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
   constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
-  // K is pre-multiplied by c = scale*log2(e) and the S accumulators start at
-  // -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the exponent
-  // c*s - LSE*log2(e) itself: no multiply-add per score (a bias then adds
-  // bias*log2(e), and a zero bias changes nothing).
-  constexpr bool PRE = FA_BWD_PRESCALE;
+  // fp16: K is pre-multiplied by c = scale*log2(e) and the S accumulators
+  // start at -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the
+  // exponent c*s - LSE*log2(e) itself: no multiply-add per score (a bias then
+  // adds bias*log2(e), and a zero bias changes nothing).  bf16 keeps the
+  // scale in fp32: rounding K*c to 8 bits tripled the gradient error at
+  // scale 1 (1.6e-2 against 5e-3; fp16: 2e-3).
+  constexpr bool PRE = FA_BWD_PRESCALE && !BF16;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -498,9 +500,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   static_assert(LOADS * kBwdThreads == BK * CPR, "tile split");
   constexpr int STAGE = dq_stage_bytes<D>();
   constexpr int TILE = BK * ROWB;
-  // Q is pre-multiplied by c and the S accumulators start at -LSE*log2(e)
-  // (this lane's row), as in the dK/dV kernel.
-  constexpr bool PRE = FA_BWD_PRESCALE;
+  // fp16: Q is pre-multiplied by c and the S accumulators start at
+  // -LSE*log2(e) (this lane's row), as in the dK/dV kernel.
+  constexpr bool PRE = FA_BWD_PRESCALE && !BF16;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 

@@ -65,6 +65,19 @@ def test_small_shapes(N, d, causal, fmt, out_f32):
     check_heads(w, res, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("fmt", [si.FMT_F16, si.FMT_BF16])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [1.0, 0.3, 0.01])
+def test_non_default_scales(scale, causal, fmt):
+    """Softmax scales other than 1/sqrt(d), forward and backward: a sharp
+    softmax (scale 1: scores with std 8), a moderate one and a nearly flat
+    one (scale 0.01)."""
+    w = si.random_case(1, 2, 200, 64, fmt, causal, seed=int(scale * 1000) + 3, with_do=True,
+                       scale=scale)
+    res = run_fwd_bwd(w)
+    check_heads(w, res, [(0, 0), (0, 1)])
+
+
 def test_long_causal_bwd_sampled():
     """Backward at the long-sequence causal shape (B=1 H=8 N=32768 d=64 bf16,
     N(0, 0.5^2), dO likewise): dQ on the sampled query rows of every head, dK
