@@ -93,6 +93,10 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * order of that section), dQ (each workgroup keeps a query tile and loops
  * over K/V tiles).
  * No atomics: results are deterministic.
+ * Accuracy: with fp16 inputs the recomputed exponent uses K (dK/dV) and Q
+ * (dQ) multiplied by scale*log2(e) and rounded to fp16 (at most 2^-11
+ * relative per element, the order of the rounding of P and dS that the
+ * 16-bit matrix products need); bf16 inputs keep the scale in fp32.
  *
  *   q, k, v, o, lse : as produced for / by flash_attn_fwd (read)
  *   dout            : [B,H,N,d] gradient of O, of the input type (read)
