@@ -26,7 +26,12 @@
  *    {64, 128, 256} for the forward entry points and {64, 128} for the
  *    backward ones (page 2, "工程落地的关键考量", hardware
  *    requirements, names 64, 128 and 256 as the preferred head sizes; no
- *    d=256 backward is provided); B*H*N*d < 2^31 elements per tensor.
+ *    d=256 backward is provided); B*H*N*d < 2^31 elements per tensor, and
+ *    (N + 256) * d * s < 2^32 bytes for every per-head output with elements
+ *    of s bytes (s = 4 for a float32 O and for the split-KV partials, 2 for
+ *    16-bit O, dQ, dK, dV): the kernels address a head through a 32-bit byte
+ *    range, including the dropped stores of a ragged last tile.  Shapes
+ *    beyond either limit return FA_ERR_SHAPE before anything is launched.
  *  - Causal: key j is visible to query i iff j <= i (queries and keys share the
  *    same length N).
  *  - Arithmetic: fp16 or bf16 operands, float32 accumulation and softmax state,
@@ -45,7 +50,9 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL                       */
-  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a tensor exceeds 2^31 elements  */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, a tensor of 2^31 elements or more,
+                           a per-head output range of 2^32 bytes or more, or
+                           causal not 0/1                                     */
   FA_ERR_HEADDIM = 3,   /* d not in {64,128,256} (fwd) or {64,128} (bwd)    */
   FA_ERR_DTYPE = 4,     /* unknown fa_dtype                                 */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                 */

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      const uint32_t off = (uint32_t)((key * D + dc * 16 + 8 * h) * 2);
+      const uint32_t off = ((uint32_t)key * D + dc * 16 + 8 * h) * 2u;
       kf[dc] = bload16(rk, off, 0);
       vf[dc] = bload16(rv, off, 0);
     }
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   const int qt_begin = CAUSAL ? (kvt * kDkvKeys) / BQ : 0;
 
   auto issue_tile = [&](int qt, char* stage) {
-    const uint32_t soff = (uint32_t)(qt * BQ * ROWB);
+    const uint32_t soff = (uint32_t)qt * (uint32_t)(BQ * ROWB);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (i * kBwdThreads + wave * 64) * 16;
@@ -303,8 +303,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     }
     // 64 LSE2 and 64 D values: 16 lanes of waves 0 and 1.
     if (lane < 16) {
-      if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
-      if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)(qt * BQ * 4));
+      if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
+      if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
     }
     if constexpr (BIAS) {
       // bias rows qt*BQ .. +63, columns of this workgroup's 128 keys: slot p
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       for (int i = 0; i < kDkvBiasBytes / 16 / kBwdThreads; ++i) {
         const int p = i * kBwdThreads + tid;
         const uint32_t off =
-            (uint32_t)(((qt * BQ + p / 16) * N + kvt * kDkvKeys + (p % 16) * 8) * 2);
+            ((uint32_t)(qt * BQ + p / 16) * (uint32_t)N + (uint32_t)(kvt * kDkvKeys + (p % 16) * 8)) * 2u;
         bload16_lds(rb, stage + BIAS_OFF + (i * kBwdThreads + wave * 64) * 16, off, 0u);
       }
     }
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   const brsrc_t rdv = make_rsrc(a.dv + base, head_bytes);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t off = (uint32_t)((key * D + dt * 32 + 16 * h) * 2);
+    const uint32_t off = ((uint32_t)key * D + dt * 32 + 16 * h) * 2u;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       u32x4 wk, wv;
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
-      const uint32_t off = (uint32_t)((qrow * D + dc * 16 + 8 * h) * 2);
+      const uint32_t off = ((uint32_t)qrow * D + dc * 16 + 8 * h) * 2u;
       qf[dc] = bload16(rq, off, 0);
       gf[dc] = bload16(rg, off, 0);
     }
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   const int n_kt = (kend + BK - 1) / BK;
 
   auto issue_tile = [&](int j, char* stage) {
-    const uint32_t soff = (uint32_t)(j * BK * ROWB);
+    const uint32_t soff = (uint32_t)j * (uint32_t)(BK * ROWB);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int slot = (i * kBwdThreads + wave * 64) * 16;
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          bw[kt][g] = bload16(rb, (uint32_t)((qrow * N + k0 + 32 * kt + 16 * g + 8 * h) * 2), 0);
+          bw[kt][g] = bload16(rb, ((uint32_t)qrow * (uint32_t)N + (uint32_t)(k0 + 32 * kt + 16 * g + 8 * h)) * 2u, 0);
     }
     f32x16 s[KT], dp[KT];
 #pragma unroll
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   const brsrc_t rdq = make_rsrc(a.dq + base, head_bytes);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t off = (uint32_t)((qrow * D + dt * 32 + 16 * h) * 2);
+    const uint32_t off = ((uint32_t)qrow * D + dt * 32 + 16 * h) * 2u;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       u32x4 w;

@@ -15,12 +15,25 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool fwd_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 bool bwd_head_dim(int d) { return d == 64 || d == 128; }
 
+// The kernels address one head's rows through a buffer resource with a 32-bit
+// byte range and 32-bit offsets, including the rows of a ragged last tile
+// past N (up to 255 of them), whose stores the range check drops.  So every
+// per-head buffer written with elements of `out_bytes` bytes must keep
+// (N + 256) * d * out_bytes below 2^32; otherwise the offsets of those tail
+// rows would wrap into the head's first rows.
+bool head_fits_u32(int N, int d, int out_bytes) {
+  return ((long long)N + 256) * d * out_bytes < (1LL << 32);
+}
+
 int check_common(int B, int H, int N, int d, float scale, int causal, int dtype, bool fwd) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
   if (!(fwd ? fwd_head_dim(d) : bwd_head_dim(d))) return FA_ERR_HEADDIM;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
   if (dtype < FA_F16 || dtype > FA_BF16_OUT_F32) return FA_ERR_DTYPE;
+  const bool o_f32 = dtype == FA_F16_OUT_F32 || dtype == FA_BF16_OUT_F32;
+  // forward: O in its output type; backward: dQ, dK, dV in the input type
+  if (!head_fits_u32(N, d, (fwd && o_f32) ? 4 : 2)) return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   return FA_OK;
@@ -116,6 +129,7 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > 64) return FA_ERR_SPLITS;
   if ((long long)num_splits * B * H * N * (d + 1) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (!head_fits_u32(N, d, 4)) return FA_ERR_SHAPE;  // float32 partial O per split and head
   if (!workspace || workspace_bytes < flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
     return FA_ERR_WORKSPACE;
   const void* ptrs[] = {q, k, v, o, lse, workspace};
@@ -293,7 +307,9 @@ const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, causal 0/1)";
+    case FA_ERR_SHAPE:
+      return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, (N+256)*d*(output element "
+             "bytes) < 2^32 per head, causal 0/1)";
     case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (forward) or 64 or 128 (backward)";
     case FA_ERR_DTYPE: return "unknown dtype code";
     case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";

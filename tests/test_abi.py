@@ -212,3 +212,35 @@ def test_bwd_bias_validation(lib, kw, status):
                 scale=0.125, causal=0, dtype=0, stream=None)
     args.update(kw)
     assert lib.flash_attn_bwd_bias(**args) == status
+
+
+# Per-head 32-bit byte ranges: (N + 256) * d * (output element bytes) must stay
+# below 2^32 (a ragged last tile's dropped stores included), although each of
+# these shapes has fewer than 2^31 elements per tensor.
+@pytest.mark.parametrize("kw", [
+    dict(N=1 << 24, d=64, dtype=2),          # fp16 in, float32 O: 2^32 + 2^16 bytes
+    dict(N=1 << 24, d=64, dtype=3),          # bf16 in, float32 O
+    dict(N=(1 << 23) - 1, d=128, dtype=2),   # just under 2^32 without the tail rows
+    dict(N=(1 << 23) - 1, d=256, dtype=0),   # 16-bit O, d=256
+])
+def test_fwd_rejects_head_range_past_2_32(lib, kw):
+    assert (1 * 1 * kw["N"] * kw["d"]) < (1 << 31)
+    assert fwd(lib, **kw) == 2
+
+
+def test_splitkv_rejects_partial_range_past_2_32(lib):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1,
+                N=1 << 24, d=64, scale=0.125, causal=0, dtype=0, num_splits=1, stream=None)
+    assert lib.flash_attn_fwd_splitkv(**args) == 2  # float32 partial O of one head
+    args.update(N=(1 << 24) - 257)  # (N + 256) * 64 * 4 < 2^32: passes, then workspace
+    assert lib.flash_attn_fwd_splitkv(**args) == 7
+
+
+def test_bwd_rejects_head_range_past_2_32(lib):
+    kw = dict(N=(1 << 24) - 1, d=128)  # (N + 256) * 128 * 2 > 2^32 for dQ, dK, dV
+    assert bwd(lib, **kw) == 2
+    args = dict(q=P, k=P, v=P, dout=P, workspace=P, workspace_bytes=1 << 20, B=1, H=1,
+                scale=0.125, causal=0, dtype=0, stream=None, **kw)
+    assert lib.flash_attn_bwd_dq(dq=P, **args) == 2
+    assert lib.flash_attn_bwd_dkdv(dk=P, dv=P, **args) == 2
+
