@@ -2,55 +2,45 @@
 the same seeded 16-bit inputs.
 
 Bounds: max|dO| <= 2e-3 (fp16) or 8e-3 (bf16) and max|dLSE| <= 1e-3.  Where O
-is stored in bf16, rounding the exact O to bf16 alone costs up to half a bf16
-ulp (7.8e-3 for |O| in [2, 4)), so there the 8e-3 bound applies to each
-element's error beyond half an ulp of the exact value; the float32-output
-variant is held to 8e-3 outright.  The spiked bf16 causal workload is gated
-on its float32-output variant, and its bf16-output run must equal the float32
-run rounded to bf16, bit for bit.
+is stored in bf16 and the exact O reaches 2 in magnitude, rounding the exact
+O to bf16 alone costs up to half a bf16 ulp (7.8e-3 for |O| in [2, 4)), so
+there the 8e-3 bound applies to each element's error beyond half an ulp of
+the exact value; everywhere else (fp16, float32 O, bf16 O below 2, and the
+long causal bf16 workload, whose O is small) it applies to the plain error.
+The spiked bf16 causal workload is gated on its float32-output variant, and
+its bf16-output run must equal the float32 run rounded to bf16, bit for bit.
 """
 import numpy as np
 import pytest
 
 import oracle
 from synth import inputs as si
-from gpu_helpers import TOL_LSE, TOL_O, f64, gated_o_error, run_fwd, dev_inputs
+from gpu_helpers import TOL_LSE, TOL_O, dev_inputs, f64, o_error, oracle_forward, run_fwd
 
 pytestmark = pytest.mark.gpu
 
 
-def check(w, o, lse, rows=None, tol_o=None, tag=""):
-    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+def check(w, o, lse, rows=None, tol_o=None, tag="", plain=False):
+    """Every element (or the listed (b, h, i) rows) against the oracle."""
     tol_o = TOL_O[w.fmt] if tol_o is None else tol_o
     og, lg = f64(o), f64(lse)
     if rows is None:
-        o_ref, l_ref = oracle.forward(q, k, v, w.scale, w.causal)
+        ref = oracle_forward(w)
+        o_ref = np.stack([np.stack([ref[(b, h)][0] for h in range(w.H)]) for b in range(w.B)])
+        l_ref = np.stack([np.stack([ref[(b, h)][1] for h in range(w.H)]) for b in range(w.B)])
     else:
+        q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
         o_ref, l_ref = oracle.forward_rows(q, k, v, rows, w.scale, w.causal)
         idx = tuple(np.array(rows).T)
         og, lg = og[idx], lg[idx]
     eo, el = np.abs(og - o_ref).max(), np.abs(lg - l_ref).max()
     bf16_store = str(o.dtype) == "torch.bfloat16"
-    gated = gated_o_error(og, o_ref, bf16_store)
-    print(f"{w.name}{tag}: max|dO|={eo:.3e}"
-          + (f" (beyond bf16 storage rounding {gated:.3e})" if bf16_store else "")
-          + f" max|dLSE|={el:.3e}", flush=True)
+    gated, how = o_error(og, o_ref, bf16_store, plain=plain)
+    print(f"{w.name}{tag}: max|dO|={eo:.3e} (checked: {how} {gated:.3e})"
+          f" max|dLSE|={el:.3e} elements={og.size}", flush=True)
     assert np.isfinite(og).all() and np.isfinite(lg).all()
-    assert gated <= tol_o, (w.name, eo, gated)
+    assert gated <= tol_o, (w.name, eo, gated, how)
     assert el <= TOL_LSE, (w.name, el)
-
-
-def sample_rows(w, count, seed):
-    rng = np.random.default_rng(seed)
-    n = w.B * w.H * w.N
-    flat = rng.choice(n, size=min(count, n), replace=False)
-    rows = {(int(f // (w.H * w.N)), int((f // w.N) % w.H), int(f % w.N)) for f in flat}
-    for b in (0, w.B - 1):
-        for h in (0, w.H - 1):
-            for i in (0, 1, 63, 64, 127, 128, 255, 256, w.N - 2, w.N - 1):
-                if 0 <= i < w.N:
-                    rows.add((b, h, i))
-    return sorted(rows)
 
 
 def test_tiny_fwd_workload():
@@ -72,32 +62,21 @@ def test_small_shapes(N, d, causal, fmt, out_f32):
     check(w, o, lse)
 
 
-@pytest.mark.parametrize("N", [1024, 2048])
+@pytest.mark.parametrize("N", [1024, 2048, 4096, 8192])
 def test_a100_shape_full(N):
-    """B=2 H=12 d=64 fp16 non-causal at the A100 table's shape, every element."""
+    """B=2 H=12 d=64 fp16 non-causal at the A100 table's shape, in the
+    benchmark's launch configuration, every element of every head."""
     w = si.a100_sweep(N)
     o, lse = run_fwd(w)
     check(w, o, lse)
 
 
-@pytest.mark.parametrize("N", [4096, 8192])
-def test_a100_shape_sampled(N):
-    """Same workload at N=4096 and 8192 in the benchmark's launch configuration,
-    checked on 1024 sampled rows plus boundary rows."""
-    w = si.a100_sweep(N)
-    o, lse = run_fwd(w)
-    check(w, o, lse, rows=sample_rows(w, 1024, N))
-
-
 def test_spiked_causal_bf16():
-    """B=2 H=16 N=4096 d=128 bf16 causal, every 64th key x8."""
+    """B=2 H=16 N=4096 d=128 bf16 causal, every 64th key x8: the float32-O run
+    on every element of all 32 heads, and the bf16-O run equal to it rounded."""
     w = si.spiked_causal()
     o32, lse = run_fwd(w, out_f32=True)
-    # full comparison on two heads, sampled rows over all heads
-    sub = si.Workload(w.name + "[heads 0,15]", 1, 2, w.N, w.d, w.fmt, True, w.scale,
-                      w.q[:1, [0, 15]], w.k[:1, [0, 15]], w.v[:1, [0, 15]])
-    check(sub, o32[:1, [0, 15]], lse[:1, [0, 15]], tag=" fp32 O")
-    check(w, o32, lse, rows=sample_rows(w, 512, 3), tag=" fp32 O sampled")
+    check(w, o32, lse, tag=" fp32 O")
     o16, lse16 = run_fwd(w, out_f32=False)
     import torch
     assert torch.equal(o16, o32.to(torch.bfloat16)), "bf16 O differs from rounded fp32 O"
@@ -105,17 +84,20 @@ def test_spiked_causal_bf16():
 
 
 def test_long_causal_sampled_rows():
-    """B=1 H=8 N=32768 d=64 bf16 N(0, 0.5^2) causal on the sampled rows."""
+    """B=1 H=8 N=32768 d=64 bf16 N(0, 0.5^2) causal on the sampled rows, O
+    stored in bf16 and held to the plain 8e-3 bound."""
     w = si.long_causal()
     o, lse = run_fwd(w)
     rows = [(0, int(h), int(i)) for h, i in si.long_causal_sample_rows(w.H, w.N)]
-    check(w, o, lse, rows=rows)
+    check(w, o, lse, rows=rows, plain=True)
 
 
 def test_long_causal_full_2048():
+    """The same distribution at N=2048, every element, plain 8e-3 bound on the
+    bf16-stored O."""
     w = si.long_causal(N=2048)
     o, lse = run_fwd(w)
-    check(w, o, lse)
+    check(w, o, lse, plain=True)
 
 
 # ----------------------------------------------------------------------------
@@ -184,11 +166,12 @@ def test_head_dim_256_full(fmt, out_f32, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_head_dim_256_sampled(causal):
-    """d=256 at B=2 H=8 N=4096 bf16 (float32 O), on sampled rows."""
+def test_head_dim_256_bench_shape(causal):
+    """d=256 at B=2 H=8 N=4096 bf16 (float32 O), the benchmarked shape, every
+    element."""
     w = si.random_case(2, 8, 4096, 256, si.FMT_BF16, causal, seed=257)
     o, lse = run_fwd(w, out_f32=True)
-    check(w, o, lse, rows=sample_rows(w, 192, 257))
+    check(w, o, lse)
 
 
 def test_errors_through_binding():
@@ -249,12 +232,12 @@ def test_splitkv_a100_shape(causal):
 
 def test_splitkv_default_splits_few_heads():
     """B=1 H=4 N=8192 d=128 bf16 (fp32 O), where the default splits the key
-    range (256 unsplit workgroups), on sampled rows."""
+    range (256 unsplit workgroups), every element."""
     import io_aware_exact_08_amd as fa
     w = si.random_case(1, 4, 8192, 128, si.FMT_BF16, False, seed=11)
     assert fa._lib.flash_attn_fwd_splitkv_default_splits(1, 4, 8192, 128, 0) == 2
     o, lse = run_splitkv(w, 0, out_f32=True)
-    check(w, o, lse, rows=sample_rows(w, 256, 11), tag=" default splits")
+    check(w, o, lse, tag=" default splits")
 
 
 def test_splitkv_long_causal_sampled():
@@ -262,7 +245,7 @@ def test_splitkv_long_causal_sampled():
     w = si.long_causal()
     o, lse = run_splitkv(w, 16)
     rows = [(0, int(h), int(i)) for h, i in si.long_causal_sample_rows(w.H, w.N)]
-    check(w, o, lse, rows=rows, tag=" splits=16")
+    check(w, o, lse, rows=rows, tag=" splits=16", plain=True)
 
 
 # ----------------------------------------------------------------------------
@@ -291,7 +274,7 @@ def check_bias(w, bias_bits, o, lse, tag=""):
     live = ~dead
     eo = np.abs(og[live] - o_ref[live]).max() if live.any() else 0.0
     el = np.abs(lg[live] - l_ref[live]).max() if live.any() else 0.0
-    gated = gated_o_error(og[live], o_ref[live], str(o.dtype) == "torch.bfloat16") if live.any() else 0.0
+    gated = o_error(og[live], o_ref[live], str(o.dtype) == "torch.bfloat16")[0] if live.any() else 0.0
     print(f"{w.name}{tag}: max|dO|={eo:.3e} max|dLSE|={el:.3e} hidden rows={int(dead.sum())}",
           flush=True)
     assert np.isfinite(og).all()
@@ -332,3 +315,26 @@ def test_bias_masks_long(kind, kw):
                       **kw)
     o, lse = run_bias(w, bb)
     check_bias(w, bb, o, lse, tag=f" {kind}")
+
+
+@pytest.mark.parametrize("kind", ["window", "leftpad"])
+def test_bias_hidden_first_tiles_low_logits_f16(kind):
+    """fp16, B=1 H=2 N=1024 d=64, non-causal.  The bias hides whole leading key
+    tiles of many rows (a band |i - j| <= 100, or every key j < 300), and each
+    visible entry carries -20, so against a reference of 0 every exponent of
+    those rows would underflow fp16.  Checked against the oracle, and against
+    the run without the -20: the same O and an LSE lower by 20 (softmax shift
+    invariance)."""
+    import torch
+    w = si.random_case(1, 2, 1024, 64, si.FMT_F16, False, seed=77)
+    i = np.arange(w.N)[:, None]
+    j = np.arange(w.N)[None, :]
+    vis = (np.abs(i - j) <= 100) if kind == "window" else (j >= 300) & (i >= 0)
+    b0 = si.f32_to_bits(np.where(vis, 0.0, -np.inf).astype(np.float32), w.fmt)
+    b20 = si.f32_to_bits(np.where(vis, -20.0, -np.inf).astype(np.float32), w.fmt)
+    o20, l20 = run_bias(w, b20)
+    check_bias(w, b20, o20, l20, tag=f" {kind} -20")
+    o0, l0 = run_bias(w, b0)
+    assert (o20.float() - o0.float()).abs().max().item() <= 2e-3
+    assert ((l20 - l0) + 20.0).abs().max().item() <= 1e-3
+    assert torch.isfinite(l20).all()
