@@ -23,24 +23,29 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 MFMA peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic_B2H12N8192d64_f16.json")
-KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hip", "io_aware_exact_08_amd/csrc/fa_bwd.hip",
-                  "io_aware_exact_08_amd/csrc/fa_device.hpp"]
+KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hpp", "io_aware_exact_08_amd/csrc/fa_fwd.hip",
+                  "io_aware_exact_08_amd/csrc/fa_bwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp"]
+# host worker processes for the CPU oracle: the GPU machine's CPU share per GPU
+MAX_CPU_WORKERS = 16
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The clocks take roughly 0.2 s of sustained load to settle; the default
-    # warm-up (about 0.3 s) covers that, so the timed steps see steady state.
+    # The clocks take roughly 0.2 s of sustained load to settle: whatever
+    # --warmup says, warm-up runs at least --warmup-s seconds of wall time
+    # (outside the timed region), so the timed steps see steady state.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=150)
+    ap.add_argument("--warmup-s", type=float, default=0.25)
     ap.add_argument("--N", type=int, default=8192)
     ap.add_argument("--causal", action="store_true")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only the forward (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=12,
-                    help="heads of the workload the CPU oracle runs for its baseline")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="worker processes for the CPU oracle (0: the usable cores, at most "
+                         f"{MAX_CPU_WORKERS})")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the "
                          "timed loop (reference dispatch for HBM byte counters)")
@@ -220,33 +225,126 @@ def config_sweep(fa, si, torch, np, dev):
     run("fwdbwd_bias_B2H12N4096d64_f16", si.fwd_bwd(False), bwd=True,
         bias_bits=si.attn_bias((2, 12, 4096, 4096), "f16", [5, 4096], "random", hole=0.1))
     run("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), bwd=True)
+    # d=128 backward at the spiked workload's shape (without the spikes)
+    run("fwdbwd_causal_B2H16N4096d128_bf16",
+        si.random_case(2, 16, 4096, 128, "bf16", True, seed=3, with_do=True), bwd=True)
+    run("fwdbwd_B2H12N4096d128_f16", si.random_case(2, 12, 4096, 128, "f16", False, seed=4,
+                                                      with_do=True), bwd=True)
+    # ragged sequence lengths around the A100 shape's largest N
+    for n in (8000, 8200):
+        run(f"fwdbwd_B2H12N{n}d64_f16", si.random_case(2, 12, n, 64, "f16", False, seed=n,
+                                                        with_do=True), bwd=True)
     run("fwd_B2H8N4096d256_f16", si.random_case(2, 8, 4096, 256, "f16", False, seed=257))
     run("fwd_causal_B2H8N4096d256_bf16_f32out", si.random_case(2, 8, 4096, 256, "bf16", True, seed=257),
         out_f32=True)
     return out
 
 
-def cpu_baseline(w, heads):
-    """The fp64 oracle as it stands, on `heads` heads of the same workload."""
-    import numpy as np
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, timed on the host cores
+# ---------------------------------------------------------------------------
+def _cpu_worker_init():
+    # one BLAS thread per worker: the pool, not BLAS, spreads the heads
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_job(job):
+    """One head (or a head's sampled rows) of the oracle, in a worker process."""
     import oracle
+    kind, a = job
+    if kind == "fwd":
+        oracle.forward_head(*a)
+    elif kind == "fwdbwd":
+        q, k, v, do, scale, causal = a
+        oracle.forward_head(q, k, v, scale, causal)
+        oracle.backward_head(q, k, v, do, scale, causal)
+    else:
+        oracle.forward_rows(*a)
+    return 0
+
+
+def _head_jobs(w, kind):
+    q, k, v = w.f64("q"), w.f64("k"), w.f64("v")
+    do = w.f64("do") if kind == "fwdbwd" else None
+    jobs = []
+    for b in range(w.B):
+        for h in range(w.H):
+            if kind == "fwd":
+                jobs.append(("fwd", (q[b, h], k[b, h], v[b, h], w.scale, w.causal)))
+            else:
+                jobs.append(("fwdbwd", (q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)))
+    return jobs
+
+
+def cpu_baseline(workers=0):
+    """The fp64 oracle as it stands (never tuned for timing), spread over a pool of
+    worker processes with one BLAS thread each, on every synthetic configuration:
+    the forward of the small, A100-shape, spiked and long causal workloads, and
+    forward+backward of the fwd+bwd workload and of the benchmarked step's own
+    workload (which gives `value`).  Credited flops as for the GPU (forward
+    4*N^2*d per head, backward 2.5x that, halved for causal).  Runs before the
+    GPU is touched, so the pool can fork."""
+    import multiprocessing as mp
+
+    import numpy as np
+    from synth import inputs as si
+
+    usable = len(os.sched_getaffinity(0))
+    k = workers or min(MAX_CPU_WORKERS, usable)
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
-    q, k, v, do = (w.f64(n) for n in ("q", "k", "v", "do"))
-    t0 = time.perf_counter()
-    for idx in range(heads):
-        b, h = divmod(idx, w.H)
-        oracle.forward_head(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
-        oracle.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
-    dt = time.perf_counter() - t0
-    flops = 3.5 * 4.0 * w.N * w.N * w.d * heads * (0.5 if w.causal else 1.0)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads, forward+backward in float64 "
-                      f"({dt:.1f} s), credited flops as for the GPU"}
+        blas = None
+    per = {}
+    with mp.get_context("fork").Pool(k, initializer=_cpu_worker_init) as pool:
+        def timed(jobs):
+            t0 = time.perf_counter()
+            pool.map(_oracle_job, jobs, chunksize=1)
+            return time.perf_counter() - t0
+
+        def heads(name, w, kind):
+            dt = timed(_head_jobs(w, kind))
+            fl = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+            fl *= 3.5 if kind == "fwdbwd" else 1.0
+            per[name] = {"seconds": round(dt, 3), "tflops": round(fl / dt / 1e12, 5),
+                         "sample": f"all {w.B * w.H} heads, {'forward+backward' if kind == 'fwdbwd' else 'forward'}"}
+            return dt, fl
+
+        heads("fwd_B1H4N128d64_f16", si.tiny_fwd(), "fwd")
+        for n in (1024, 2048, 4096, 8192):
+            heads(f"fwd_B2H12N{n}d64_f16", si.a100_sweep(n), "fwd")
+        heads("fwd_causal_B2H16N4096d128_bf16_spiked", si.spiked_causal(), "fwd")
+        # long causal: the sampled rows, then every row at N=2048
+        w = si.long_causal()
+        pairs = si.long_causal_sample_rows(w.H, w.N)
+        q, kk, v = w.f64("q"), w.f64("k"), w.f64("v")
+        jobs = []
+        for h in sorted({int(h) for h, _ in pairs}):
+            rows = [(0, 0, int(i)) for hh, i in pairs if hh == h]
+            jobs.append(("rows", (q[:, h:h + 1], kk[:, h:h + 1], v[:, h:h + 1], rows, w.scale, True)))
+        dt = timed(jobs)
+        fl_rows = sum(4.0 * (int(i) + 1) * w.d for _, i in pairs)
+        full = 4.0 * w.H * w.N * w.N * w.d * 0.5
+        per["fwd_causal_B1H8N32768d64_bf16_rows"] = {
+            "seconds": round(dt, 3), "rows": int(len(pairs)), "rows_per_s": round(len(pairs) / dt, 1),
+            "tflops": round(fl_rows / dt / 1e12, 5),
+            "full_forward_s_extrapolated": round(full / (fl_rows / dt), 1),
+            "sample": f"{len(pairs)} sampled query rows over 8 heads at N=32768 (the full "
+                      "forward's time is extrapolated from their flop rate)"}
+        heads("fwd_causal_B1H8N2048d64_bf16", si.long_causal(N=2048), "fwd")
+        heads("fwdbwd_B2H12N4096d64_f16", si.fwd_bwd(False), "fwdbwd")
+        heads("fwdbwd_causal_B2H12N4096d64_f16", si.fwd_bwd(True), "fwdbwd")
+        dt, fl = heads("fwdbwd_B2H12N8192d64_f16", si.a100_sweep(8192, with_do=True), "fwdbwd")
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": k, "kind": "oracle",
+            "sample": f"the benchmarked step's workload (B2 H12 N8192 d64 fp16), all 24 heads, "
+                      f"forward+backward in float64 ({dt:.1f} s), credited flops as for the GPU",
+            "workers": k, "usable_cores": usable, "blas_threads_per_worker": 1,
+            "blas_threads_default": blas, "per_config": per}
 
 
 def main():
@@ -260,6 +358,10 @@ def main():
               "(the path shards by heads with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    # The CPU oracle runs first, before anything touches the GPU, so that its
+    # worker pool can fork.
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_workers)
 
     import numpy as np
     import torch
@@ -309,9 +411,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    # Warm-up: at least --warmup steps and at least --warmup-s seconds of wall
+    # time (the clocks settle after about 0.2 s of sustained load).
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_s:
         step()
+        n_warm += 1
+        if n_warm % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -322,6 +432,10 @@ def main():
 
     def avg_ms(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
+
+    last = 1 if args.fwd_only else 4
+    per_step = np.array([e[0].elapsed_time(e[last]) for e in events])
+    q25, med, q75 = (float(x) for x in np.percentile(per_step, [25, 50, 75]))
 
     ms_per_step = wall * 1e3 / args.steps
     causal_f = 0.5 if w.causal else 1.0
@@ -353,6 +467,10 @@ def main():
             "accumulate": "f32", "parallelism": "single GPU",
         },
         "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
+        "step_ms_events": {"median": round(med, 4), "q25": round(q25, 4), "q75": round(q75, 4),
+                           "iqr": round(q75 - q25, 4), "mean": round(float(per_step.mean()), 4)},
+        "tflops_at_median_step": round(step_flops / (med * 1e-3) / 1e12, 2),
+        "warmup_done": {"steps": n_warm, "seconds": round(warm_s, 3)},
         "fwd": {"ms": round(fwd_avg, 4), "tflops": round(fwd_tflops, 2),
                 "frac_of_peak": round(fwd_tflops / PEAK_MFMA_F16_TFLOPS, 4)},
     }
@@ -385,8 +503,8 @@ def main():
     }
     if not args.no_sweep:
         res["configs"] = config_sweep(fa, si, torch, np, dev)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
