@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 MFMA peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic_B2H12N8192d64_f16.json")
 KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hpp", "io_aware_exact_08_amd/csrc/fa_fwd.hip",
-                  "io_aware_exact_08_amd/csrc/fa_bwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp"]
+                  "io_aware_exact_08_amd/csrc/fa_bwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp",
+                  "io_aware_exact_08_amd/csrc/flash_attn_api.hip"]
 # host worker processes for the CPU oracle: the GPU machine's CPU share per GPU
 MAX_CPU_WORKERS = 16
 

@@ -15,8 +15,11 @@
  *  - Pointers are DEVICE pointers (HIP global memory) of the calling process's
  *    current device.  Every tensor pointer must be 16-byte aligned.
  *  - Ownership: the caller allocates and frees every buffer.  The library never
- *    allocates device memory and keeps no mutable global state; calls are
- *    thread-safe.  Inputs are read-only; outputs are fully overwritten.
+ *    allocates device memory.  Its only global state belongs to
+ *    flash_attn_bwd_noalloc: a static device array and the per-device address
+ *    of it, set once under a lock.  Calls are thread-safe (apart from that
+ *    entry point's shared array, see there).  Inputs are read-only; outputs
+ *    are fully overwritten.
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and the call returns before it runs.  Faults inside the kernels
  *    surface at the caller's next synchronisation.
@@ -59,7 +62,9 @@ typedef enum {
   FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */
   FA_ERR_WORKSPACE = 7, /* workspace missing or too small                   */
   FA_ERR_SCALE = 8,     /* scale is not a finite positive number            */
-  FA_ERR_SPLITS = 9     /* num_splits outside [1, 64]                       */
+  FA_ERR_SPLITS = 9,    /* num_splits outside [1, 64]                       */
+  FA_ERR_SCRATCH = 10   /* flash_attn_bwd_noalloc: the problem's workspace
+                           exceeds FA_NOALLOC_SCRATCH_BYTES                  */
 } fa_status;
 
 /* Element types: Q/K/V (and dQ/dK/dV) type x O (and dO) type. */
@@ -223,6 +228,30 @@ int flash_attn_fwd_splitkv_default_splits(int B, int H, int N, int d, int causal
 /* Bytes of workspace flash_attn_bwd needs (8 * B * H * N: two floats per row,
  * -D and -LSE*log2(e)); 0 for invalid sizes. */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation.  Same computation, kernels, arguments, checks and
+ * results (bit for bit) as flash_attn_bwd, without the workspace arguments:
+ * its -D and -LSE*log2(e) rows live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every device it
+ * runs on until the process ends (the address is looked up once per device,
+ * on the first call with that device current).  The call itself allocates
+ * nothing; the caller still provides every input and output.
+ *   Limit: 8 * B * H * N <= FA_NOALLOC_SCRATCH_BYTES (B*H*N <= 2,097,152
+ *   rows), else FA_ERR_SCRATCH before anything is launched.
+ *   Concurrency: all calls on one device share that device's array, so calls
+ *   whose work overlaps in time on one device (different streams, or host
+ *   threads without ordering) race and give wrong gradients; calls ordered on
+ *   one stream are safe.  Each call rewrites every row it reads, so nothing
+ *   left by an earlier call is used.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, float scale, int causal, int dtype,
+                           void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* flash_attn_status_string(int status);

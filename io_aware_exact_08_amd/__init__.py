@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import FlashAttnError, status_string  # noqa: F401
 
 __all__ = ["flash_attn_fwd", "flash_attn_fwd_bias", "flash_attn_fwd_splitkv", "flash_attn_bwd",
-           "flash_attn_bwd_bias", "flash_attn_bwd_preprocess",
+           "flash_attn_bwd_bias", "flash_attn_bwd_noalloc", "flash_attn_bwd_preprocess",
            "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "FlashAttnError", "status_string",
            "dtype_code", "workspace_bytes"]
 
@@ -188,6 +188,36 @@ def flash_attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None,
                              B, H, N, d, sc, int(bool(causal)), code, _stream(q))
     if st != _lib.FA_OK:
         raise FlashAttnError(st, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, causal: bool = False, scale=None,
+                           dq=None, dk=None, dv=None):
+    """flash_attn_bwd without a workspace argument: the library keeps the
+    per-row terms in its static device scratch (8*B*H*N bytes must fit it).
+    The C call allocates nothing; dq/dk/dv are allocated here unless given."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    out_f32 = o.dtype == torch.float32
+    _check(o, "o", (B, H, N, d), o.dtype)
+    if not out_f32 and o.dtype != q.dtype:
+        raise TypeError("o must have the input dtype or float32")
+    _check(lse, "lse", (B, H, N), torch.float32)
+    code = dtype_code(q.dtype, out_f32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(t, name, (B, H, N, d), q.dtype)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    st = _lib.flash_attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                     dv.data_ptr(), B, H, N, d, sc, int(bool(causal)), code,
+                                     _stream(q))
+    if st != _lib.FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_noalloc")
     return dq, dk, dv
 
 

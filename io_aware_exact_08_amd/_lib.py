@@ -13,6 +13,8 @@ LIB_PATH = os.path.join(_PKG, "libflash_attn.so")
 
 FA_OK = 0
 FA_F16, FA_BF16, FA_F16_OUT_F32, FA_BF16_OUT_F32 = 0, 1, 2, 3
+FA_ERR_SCRATCH = 10
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # FA_NOALLOC_SCRATCH_BYTES in the header
 
 # every extern "C" symbol declared in include/flash_attn.h
 EXPORTED = (
@@ -27,6 +29,7 @@ EXPORTED = (
     "flash_attn_bwd_dkdv",
     "flash_attn_bwd_dq",
     "flash_attn_bwd_workspace_bytes",
+    "flash_attn_bwd_noalloc",
     "flash_attn_status_string",
     "flash_attn_version",
 )
@@ -74,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.flash_attn_bwd_dkdv.restype = i
     lib.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
     lib.flash_attn_bwd_dq.restype = i
+    lib.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_bwd_noalloc.restype = i
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_status_string.argtypes = [i]
@@ -149,6 +154,13 @@ def flash_attn_bwd_dq(q, k, v, dout, workspace, workspace_bytes, dq, B, H, N, d,
                       dtype, stream) -> int:
     return load().flash_attn_bwd_dq(q, k, v, dout, workspace, workspace_bytes, dq, B, H, N, d,
                                     float(scale), int(causal), int(dtype), stream)
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, dtype,
+                           stream) -> int:
+    """Raw C call with integer device pointers; returns the fa_status."""
+    return load().flash_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d,
+                                         float(scale), int(causal), int(dtype), stream)
 
 
 def flash_attn_bwd_workspace_bytes(B, H, N, d) -> int:

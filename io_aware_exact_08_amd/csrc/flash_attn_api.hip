@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/flash_attn.h"
 #include "fa_launch.hpp"
 
@@ -303,6 +305,83 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
   return fa::launch_bwd_dq(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace of flash_attn_bwd (-D and
+// -LSE*log2(e), two floats per row) in a static device array.
+// ---------------------------------------------------------------------------
+namespace {
+
+static_assert(FA_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+// One copy per device, alive until the process ends.  In host code `scratch`
+// names a host-side handle, not a device address: kernels get the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_addr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                           int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_common(B, H, N, d, scale, causal, dtype, false);
+  if (st != FA_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * N;
+  if (2 * rows * sizeof(float) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  fa::BwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  // Every row's -D and -LSE*log2(e) are written by the preprocess before the
+  // other two kernels read them, so nothing needs clearing between calls.
+  p.delta = (float*)ws;
+  p.lse2 = (float*)ws + rows;
+  p.BH = B * H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal != 0;
+  p.dtype = dtype;
+  return fa::launch_bwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* flash_attn_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -317,6 +396,9 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_SPLITS: return "num_splits must be between 1 and 64";
+    case FA_ERR_SCRATCH:
+      return "problem too large for the allocation-free entry point's static scratch "
+             "(8 * B * H * N bytes must fit FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

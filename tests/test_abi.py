@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
         "flash_attn_fwd_splitkv_default_splits", "flash_attn_bwd", "flash_attn_bwd_bias",
         "flash_attn_bwd_preprocess",
         "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_workspace_bytes",
-        "flash_attn_status_string", "flash_attn_version"])
+        "flash_attn_bwd_noalloc", "flash_attn_status_string", "flash_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.flash_attn_version() >= 102
     assert lib.status_string(0) == "ok"
-    for st in range(1, 10):
+    for st in range(1, 11):
         assert lib.status_string(st) not in ("ok", "unknown status")
     assert lib.status_string(99) == "unknown status"
 
@@ -244,3 +244,27 @@ def test_bwd_rejects_head_range_past_2_32(lib):
     assert lib.flash_attn_bwd_dq(dq=P, **args) == 2
     assert lib.flash_attn_bwd_dkdv(dk=P, dv=P, **args) == 2
 
+
+def noalloc(lib, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, H=1, N=8, d=64,
+                scale=0.125, causal=0, dtype=0, stream=None)
+    args.update(kw)
+    return lib.flash_attn_bwd_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), 1), (dict(dq=None), 1), (dict(N=0), 2), (dict(N=(1 << 24) - 1, d=128), 2),
+    (dict(d=256), 3), (dict(dtype=8), 4), (dict(dk=P + 8), 5), (dict(scale=0.0), 8),
+    # the static scratch holds 8 bytes per row: 2^21 rows fit, one more does not
+    (dict(B=1, H=32, N=65537), 10), (dict(B=2, H=1, N=(1 << 20) + 1), 10),
+])
+def test_bwd_noalloc_validation(lib, kw, status):
+    """Every rejection happens before the scratch address is looked up, so no
+    HIP call is made."""
+    assert noalloc(lib, **kw) == status
+
+
+def test_noalloc_limit_matches_header(lib):
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)" in text
+    assert lib.NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
