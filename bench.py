@@ -23,9 +23,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 MFMA peak
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic_B2H12N8192d64_f16.json")
-KERNEL_SOURCES = ["io_aware_exact_08_amd/csrc/fa_fwd.hpp", "io_aware_exact_08_amd/csrc/fa_fwd.hip",
-                  "io_aware_exact_08_amd/csrc/fa_bwd.hip", "io_aware_exact_08_amd/csrc/fa_device.hpp",
-                  "io_aware_exact_08_amd/csrc/flash_attn_api.hip"]
+# every HIP source and header of the library (a stored counter summary counts
+# only for the sources it was taken on)
+KERNEL_SOURCES = sorted(os.path.join("io_aware_exact_08_amd", "csrc", f)
+                        for f in os.listdir(os.path.join(ROOT, "io_aware_exact_08_amd", "csrc"))
+                        if f.endswith((".hip", ".hpp")))
 # host worker processes for the CPU oracle: the GPU machine's CPU share per GPU
 MAX_CPU_WORKERS = 16
 
@@ -235,9 +237,10 @@ def config_sweep(fa, si, torch, np, dev):
     for n in (8000, 8200):
         run(f"fwdbwd_B2H12N{n}d64_f16", si.random_case(2, 12, n, 64, "f16", False, seed=n,
                                                         with_do=True), bwd=True)
-    run("fwd_B2H8N4096d256_f16", si.random_case(2, 8, 4096, 256, "f16", False, seed=257))
-    run("fwd_causal_B2H8N4096d256_bf16_f32out", si.random_case(2, 8, 4096, 256, "bf16", True, seed=257),
-        out_f32=True)
+    run("fwdbwd_B2H8N4096d256_f16", si.random_case(2, 8, 4096, 256, "f16", False, seed=257,
+                                                     with_do=True), bwd=True)
+    run("fwdbwd_causal_B2H8N4096d256_bf16_f32out",
+        si.random_case(2, 8, 4096, 256, "bf16", True, seed=257, with_do=True), out_f32=True, bwd=True)
     return out
 
 

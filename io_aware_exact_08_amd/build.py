@@ -24,12 +24,19 @@ LIB = os.path.join(PKG, "libflash_attn.so")
 OBJDIR = os.path.join(ROOT, "_build")
 RESOURCES = os.path.join(PKG, "kernel_resources.json")
 
-# (object name, source, extra defines)
-UNITS = [("flash_attn_api", "flash_attn_api.hip", []),
-         ("fa_fwd", "fa_fwd.hip", []),
-         ("fa_bwd", "fa_bwd.hip", [])]
-UNITS += [(f"fa_fwd_inst_{d}_{k}", "fa_fwd_inst.hip", [f"-DFA_INST_D={d}", f"-DFA_INST_KIND={k}"])
+# The d=256 backward keeps its dK/dV (and dQ) accumulators, 256 (128)
+# registers per lane, in the accumulation registers: it is compiled without
+# the flag that restricts MFMA accumulators to the ordinary VGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+# (object name, source, extra defines, flags removed for this unit)
+UNITS = [("flash_attn_api", "flash_attn_api.hip", [], []),
+         ("fa_fwd", "fa_fwd.hip", [], []),
+         ("fa_bwd", "fa_bwd.hip", [], [])]
+UNITS += [(f"fa_fwd_inst_{d}_{k}", "fa_fwd_inst.hip", [f"-DFA_INST_D={d}", f"-DFA_INST_KIND={k}"], [])
           for d in (64, 128, 256) for k in (0, 1, 2)]
+UNITS += [(f"fa_bwd_inst_{d}", "fa_bwd_inst.hip", [f"-DFA_INST_D={d}"], VGPR_FORM if d == 256 else [])
+          for d in (64, 128, 256)]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -40,7 +47,7 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
     # MFMA accumulators in VGPRs (no AGPR copies around the softmax)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    *VGPR_FORM,
     # no NaN canonicalisation in max (infinities are still honoured)
     "-fno-honor-nans",
 ]
@@ -98,10 +105,19 @@ def demangle(names):
     return dict(zip(names, dem)) if len(dem) == len(names) else {n: n for n in names}
 
 
+def _remove(flags, drop):
+    """flags without the consecutive sequence `drop` (if present)."""
+    n = len(drop)
+    for i in range(len(flags) - n + 1):
+        if n and flags[i:i + n] == drop:
+            return flags[:i] + flags[i + n:]
+    return list(flags)
+
+
 def _compile(unit, extra_flags, verbose):
-    name, src, defs = unit
+    name, src, defs, drop = unit
     obj = os.path.join(OBJDIR, name + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + defs + \
+    cmd = [hipcc()] + _remove(HIPCC_FLAGS, drop) + list(extra_flags) + defs + \
         ["-Rpass-analysis=kernel-resource-usage", "-I", os.path.join(ROOT, "include"),
          "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
@@ -137,10 +153,12 @@ def build(verbose: bool = False, extra_flags=None, jobs: int | None = None) -> s
     rec = {"sources_sha256_16": sources_digest(extra_flags),
            "flags": HIPCC_FLAGS + extra_flags,
            "kernels": {names[k]: kernels[k] for k in sorted(kernels, key=lambda k: names[k])}}
-    if not extra_flags:  # the summary describes the shipped flags only
-        with open(RESOURCES, "w") as f:
-            json.dump(rec, f, indent=1, sort_keys=False)
-            f.write("\n")
+    # the tracked summary describes the shipped flags only; other flags write
+    # theirs beside their objects
+    out = RESOURCES if not extra_flags else os.path.join(OBJDIR, "kernel_resources.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=False)
+        f.write("\n")
     if verbose:
         spills = [(n, r) for n, r in rec["kernels"].items()
                   if r.get("vgpr_spill", 0) or r.get("sgpr_spill", 0) or r.get("scratch_bytes_per_lane", 0)]

@@ -1,819 +1,36 @@
-// Recompute-based backward of exact attention for gfx950.
-//
-// Page 2 of the subject, "Re-computation": no score or probability is kept
-// from the forward; each (query tile, key tile) block recomputes
-// S = scale Q K^T and P from it, with an outer loop over K/V column blocks and
-// an inner loop over Q row blocks.  P is rebuilt with the forward's row LSE,
-// P_ij = exp(scale q_i.k_j - LSE_i), which is the normalised softmax (the
-// block-local softmax printed on that page would not be).  Gradients of
-// L = <dO, O>:
-//   D_i = sum_c dO_ic O_ic,  dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
-//   dK = scale dS^T Q,       dQ = scale dS K.
-//
-// Three kernels, all deterministic (no atomics):
-//  * bwd_pre   : -D and -LSE*log2(e) for every row (one pass over O and dO).
-//  * bwd_dkdv  : a workgroup keeps 128 keys of K and V in registers (32 per
-//                wave) and loops over 64-row Q/dO tiles (the loop order
-//                above); dK and dV accumulate in registers.
-//  * bwd_dq    : a workgroup keeps 128 query rows of Q and dO in registers and
-//                loops over 64-key K/V tiles.
-// Mapping onto CDNA4, as in the forward: v_mfma_f32_32x32x16 with the
-// accumulator of one product feeding the next as its B operand after
-// rounding; streamed tiles arrive by direct buffer->LDS loads into two
-// stages; operands that contract over tile rows are read with the
-// transposing ds_read_b64_tr_b16 from the same row-major tile (one XOR
-// swizzle serves both read patterns); the dP accumulator starts at -D so
-// the MFMA produces dP - D; tiles on the causal diagonal run a masked copy of
-// the tile body.  Rows and keys past N read as zeros and contribute nothing
-// (their dO or K/V rows are zero), and stores past N are dropped.
-#include <type_traits>
-
-#include "fa_device.hpp"
-#include "fa_launch.hpp"
+// Backward dispatch over head dimension.  The kernels are in fa_bwd.hpp and
+// are instantiated per head dimension by fa_bwd_inst.hip.
+#include "fa_bwd.hpp"
 
 namespace fa {
 
-constexpr int kBwdThreads = 256;
-
-// ---------------------------------------------------------------------------
-// -D_i = -sum_c dO_ic O_ic and -LSE_i * log2(e)
-// ---------------------------------------------------------------------------
-template <int D, bool BF16, bool O_F32>
-__global__ __launch_bounds__(kBwdThreads) void bwd_pre_kernel(const void* __restrict__ o,
-                                                              const uint16_t* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              float* __restrict__ delta,
-                                                              float* __restrict__ lse2, int rows) {
-  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
-  constexpr int RPB = kBwdThreads / LPR;
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * RPB + tid / LPR;
-  const int c = tid % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + c * 8;
-    const u32x4 g = *(const u32x4*)(dout + off);
-    float gv[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gv[2 * e] = to_f32<BF16>((uint16_t)(g[e] & 0xffffu));
-      gv[2 * e + 1] = to_f32<BF16>((uint16_t)(g[e] >> 16));
-    }
-    if constexpr (O_F32) {
-      const f32x4 o0 = *(const f32x4*)((const float*)o + off);
-      const f32x4 o1 = *(const f32x4*)((const float*)o + off + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc += gv[e] * o0[e] + gv[4 + e] * o1[e];
-    } else {
-      const u32x4 ov = *(const u32x4*)((const uint16_t*)o + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += gv[2 * e] * to_f32<BF16>((uint16_t)(ov[e] & 0xffffu));
-        acc += gv[2 * e + 1] * to_f32<BF16>((uint16_t)(ov[e] >> 16));
-      }
-    }
-  }
-#pragma unroll
-  for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w, 64);
-  if (row < rows && c == 0) {
-    // Both stored negated: they seed the dP - D and c*s - LSE*log2(e)
-    // accumulators as they are.  A row whose every key is hidden (LSE = -inf,
-    // O = 0) must recompute P = 0: its exponent reference is -inf.
-    delta[row] = -acc;
-    lse2[row] = lse[row] == -INFINITY ? -INFINITY : -(lse[row] * kLog2e);
-  }
-}
-
-struct BwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const uint16_t* dout;
-  const float* lse2;   // -LSE * log2(e)
-  const float* delta;  // -D
-  uint16_t* dq;
-  uint16_t* dk;
-  uint16_t* dv;
-  int N;
-  int BH;
-  int n_tiles;  // workgroup tiles per head
-  float c;      // scale * log2(e)
-  float scale;
-  // additive attention bias (as in the forward), or null
-  const uint16_t* bias;
-  long long bias_sb, bias_sh;
-  int H;
-};
-
-// Per-lane byte offsets shared by both kernels for a row-major LDS tile with
-// ROWB bytes per row, swizzled with swz_dual (read both as a row operand and
-// through the transposing read).
-template <int D>
-struct TileOffsets {
-  static constexpr int ROWB = D * 2;
-  static constexpr int DC = D / 16;
-  static constexpr int DT = D / 32;
-  int rd[DC];   // row operand: rows 32t + perm_k(m), chunk 2dc+h (+ 32t*ROWB)
-  int trl[DT];  // transposing read for d tile dt, k-rows 8h + j (+ 16kc*ROWB)
-  int trh[DT];  // the same for k-rows 8h + 4 + j
-  __device__ __forceinline__ TileOffsets(int lane) {
-    const int m = lane & 31, h = lane >> 5;
-    const int row = perm_k(m);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) rd[dc] = row * ROWB + (((2 * dc + h) ^ swz_dual<D>(row)) * 16);
-    const int i = lane & 15, gg = (lane >> 4) & 1;
-    const int j = i >> 2, q = i & 3;
-    const int trow = 8 * h + j;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int chunk = 4 * dt + 2 * (q & 1) + gg;
-      trl[dt] = trow * ROWB + ((chunk ^ swz_dual<D>(trow)) * 16) + (q >> 1) * 8;
-      trh[dt] = (trow + 4) * ROWB + ((chunk ^ swz_dual<D>(trow + 4)) * 16) + (q >> 1) * 8;
-    }
-  }
-};
-
-// Direct-load slot p = i*256 + tid of a tile of rows x CPR 16-byte chunks:
-// tile row p / CPR at swizzled chunk position p % CPR.
-template <int D>
-__device__ __forceinline__ uint32_t tile_src_offset(int p) {
-  constexpr int CPR = D / 8;
-  const int row = p / CPR, cpos = p % CPR;
-  return (uint32_t)(row * D * 2 + ((cpos ^ swz_dual<D>(row)) * 16));
-}
-
-// Transposed operand (A of an O^T-shaped product) for 16 k-rows starting at
-// tile row 16*kc from the transposing reads.
-__device__ __forceinline__ u32x4 tr_operand(const char* tile, int off_lo, int off_hi, int kc,
-                                            int rowb) {
-  const u32x2 lo = lds_read_tr16(tile + off_lo + kc * 16 * rowb);
-  const u32x2 hi = lds_read_tr16(tile + off_hi + kc * 16 * rowb);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
-template <int D>
-constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
-
-// Operand reads issued this many MFMAs ahead of their MFMA (pin_step).  Left
-// to itself the scheduler hoists a tile's transposing reads far ahead: the
-// causal dK/dV instantiations reached 320 live registers before allocation
-// and spilled 16.  Measured on MI355X, lookahead 4 against none: causal
-// dK/dV -23% (N=4096) and -20% (N=32768), non-causal dK/dV -1%, dQ -1.5%
-// (non-causal) to -7% (causal N=4096); lookahead 2, 6 and 8 were slower.
-// With the log2-unit scores (fewer VALU instructions per tile) lookahead 3
-// beat 4 on every backward shape measured: dK/dV -0.8% (B2 H12 N8192 fp16),
-// -2.4% (causal N=4096), -0.9% (B1 H8 N32768 bf16 causal), dQ -0.4 to -1.1%;
-// 5 and 6 were not faster than 4.
-#ifndef FA_BWD_PIN_LA
-#define FA_BWD_PIN_LA 3
-#endif
-// Order of the second product chain (dV/dK, dQ): contraction chunk outermost,
-// so its first half needs only the first 32-row half of P and dS and the
-// second half's exponentials can run under those MFMAs.  Measured on MI355X
-// against d-tile outermost: causal dK/dV -1.7% (B2 H12 N4096 fp16), dQ -1.5%
-// (B1 H8 N32768 bf16 causal) and -0.5% (B2 H12 N8192 fp16), others unchanged.
-#ifndef FA_BWD_PRESCALE
-#define FA_BWD_PRESCALE 1
-#endif
-#ifndef FA_BWD_CHUNK_MAJOR
-#define FA_BWD_CHUNK_MAJOR 1
-#endif
-
-// ---------------------------------------------------------------------------
-// dK, dV: workgroup owns 128 keys (32 per wave); loop over 64-row query tiles.
-// ---------------------------------------------------------------------------
-constexpr int kDkvKeys = 128;  // keys per workgroup
-constexpr int kDkvBQ = 64;     // query rows per streamed tile
-
-template <int D>
-__host__ __device__ constexpr int dkdv_stage_bytes() {
-  return 2 * kDkvBQ * D * 2 + 2 * kDkvBQ * 4;  // Q, dO tiles + LSE2, D rows
-}
-// With an attention bias a stage also holds the bias block of the tile's 64
-// query rows x the workgroup's 128 keys (row-major, 256 bytes per row).
-constexpr int kDkvBiasRowBytes = kDkvKeys * 2;
-constexpr int kDkvBiasBytes = kDkvBQ * kDkvBiasRowBytes;
-
-template <int D, bool BF16, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BQ = kDkvBQ;
-  constexpr int DC = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int QT = BQ / 32;  // 32-row query sub-tiles per streamed tile
-  constexpr int QC = BQ / 16;  // 16-row query chunks (contraction of dK, dV)
-  constexpr int CPR = D / 8;
-  constexpr int ROWB = D * 2;
-  constexpr int LOADS = BQ * CPR / kBwdThreads;
-  static_assert(LOADS * kBwdThreads == BQ * CPR, "tile split");
-  constexpr int STAGE = dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0);
-  constexpr int TILE = BQ * ROWB;
-  constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
-  // fp16: K is pre-multiplied by c = scale*log2(e) and the S accumulators
-  // start at -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the
-  // exponent c*s - LSE*log2(e) itself: no multiply-add per score (a bias then
-  // adds bias*log2(e), and a zero bias changes nothing).  bf16 keeps the
-  // scale in fp32: rounding K*c to 8 bits tripled the gradient error at
-  // scale 1 (1.6e-2 against 5e-3; fp16: 2e-3).
-  constexpr bool PRE = FA_BWD_PRESCALE && !BF16;
-
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 31, h = lane >> 5;
-
-  int bh, kvt;
-  {
-    const int bid = blockIdx.x;
-    if (CAUSAL) {
-      kvt = bid / a.BH;  // first key tiles see the most queries: issue first
-      bh = bid % a.BH;
-    } else {
-      const int G = gridDim.x;
-      const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-      bh = lin / a.n_tiles;
-      kvt = lin % a.n_tiles;
-    }
-  }
-  const int N = a.N;
-  const size_t base = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
-  const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
-  const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
-  const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
-  const brsrc_t rb =
-      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
-                BIAS ? (uint32_t)N * N * 2 : 0u);
-  // Bias gather through the transposing read: in each 16-lane group (G), lane
-  // L supplies row R + L/4 and columns c0 + 4(L%4) .. +3 of the row-major bias
-  // block; result lane i then holds rows R..R+3 of column c0 + i.  With
-  // c0 = 32*wave + 16(G%2) and R = 32t + 16g + 8(G/2) (+4), lane l receives
-  // exactly the bias of its key (32*wave + l%32) at the query rows of score
-  // registers 8g + 0..3 (and 4..7) of sub-tile t.
-  const int bias_rd = ((lane & 15) >> 2) * kDkvBiasRowBytes + 8 * ((lane >> 5) & 1) * kDkvBiasRowBytes +
-                      (32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  const int kw0 = kvt * kDkvKeys + wave * 32;  // first key of this wave
-  const int key = kw0 + m;                     // this lane's key (column of S)
-
-  // K and V as B operands (lane: key m; slot i: d = 16dc + 8h + i).
-  u32x4 kf[DC], vf[DC];
-  {
-    const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
-    const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const uint32_t off = ((uint32_t)key * D + dc * 16 + 8 * h) * 2u;
-      kf[dc] = bload16(rk, off, 0);
-      vf[dc] = bload16(rv, off, 0);
-    }
-    if constexpr (PRE) {
-      // K * c rounded to the input type once: the S MFMAs then yield c*s
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = kf[dc][e];
-          kf[dc][e] = pack2<BF16>(to_f32<BF16>((uint16_t)(w & 0xffffu)) * a.c,
-                                  to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
-        }
-    }
-  }
-  const TileOffsets<D> to(lane);
-  uint32_t src[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) src[i] = tile_src_offset<D>(i * kBwdThreads + tid);
-
-  f32x16 dkt[DT], dvt[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dkt[dt] = f32x16{};
-    dvt[dt] = f32x16{};
-  }
-
-  const int n_qt = (N + BQ - 1) / BQ;
-  const int qt_begin = CAUSAL ? (kvt * kDkvKeys) / BQ : 0;
-
-  auto issue_tile = [&](int qt, char* stage) {
-    const uint32_t soff = (uint32_t)qt * (uint32_t)(BQ * ROWB);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int slot = (i * kBwdThreads + wave * 64) * 16;
-      bload16_lds(rq, stage + slot, src[i], soff);
-      bload16_lds(rg, stage + TILE + slot, src[i], soff);
-    }
-    // 64 LSE2 and 64 D values: 16 lanes of waves 0 and 1.
-    if (lane < 16) {
-      if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
-      if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
-    }
-    if constexpr (BIAS) {
-      // bias rows qt*BQ .. +63, columns of this workgroup's 128 keys: slot p
-      // holds row p/16, 16-byte chunk p%16 (rows past N read as 0)
-#pragma unroll
-      for (int i = 0; i < kDkvBiasBytes / 16 / kBwdThreads; ++i) {
-        const int p = i * kBwdThreads + tid;
-        const uint32_t off =
-            ((uint32_t)(qt * BQ + p / 16) * (uint32_t)N + (uint32_t)(kvt * kDkvKeys + (p % 16) * 8)) * 2u;
-        bload16_lds(rb, stage + BIAS_OFF + (i * kBwdThreads + wave * 64) * 16, off, 0u);
-      }
-    }
-  };
-
-  const float c = a.c;
-  auto tile_body = [&](auto mask_tag, const char* stage, int q0) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const char* sQ = stage;
-    const char* sG = stage + TILE;
-    const float* sL = (const float*)(stage + 2 * TILE);
-    const float* sD = sL + BQ;
-    // S = Q K^T; dP - D = dO V^T - D (rows: queries with perm_k, cols: keys).
-    // Register r of sub-tile t holds query row t*32 + 16(r/8) + 8h + r%8.
-    f32x16 s[QT], dp[QT];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      s[t] = f32x16{};
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int qb = t * 32 + 16 * g + 8 * h;
-        const f32x4 d0 = *(const f32x4*)(&sD[qb]);
-        const f32x4 d1 = *(const f32x4*)(&sD[qb + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dp[t][8 * g + e] = d0[e];
-          dp[t][8 * g + 4 + e] = d1[e];
-        }
-        if constexpr (PRE) {
-          const f32x4 l0 = *(const f32x4*)(&sL[qb]);
-          const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s[t][8 * g + e] = l0[e];
-            s[t][8 * g + 4 + e] = l1[e];
-          }
-        }
-      }
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 qa = *(const u32x4*)(sQ + t * 32 * ROWB + to.rd[dc]);
-        const u32x4 ga = *(const u32x4*)(sG + t * 32 * ROWB + to.rd[dc]);
-        s[t] = mfma32<BF16>(qa, kf[dc], s[t]);
-        pin_step<1, 1, FA_BWD_PIN_LA>(2 * (t * DC + dc));
-        dp[t] = mfma32<BF16>(ga, vf[dc], dp[t]);
-        pin_step<1, 1, FA_BWD_PIN_LA>(2 * (t * DC + dc) + 1);
-      }
-    }
-    pin_tail<1, FA_BWD_PIN_LA>();
-    if constexpr (BIAS) {
-      // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e));
-      // with PRE the scores are already in log2 units: s + bias*log2(e)
-      const float kb = PRE ? kLog2e : 1.0f / a.scale;
-      const char* sB = stage + BIAS_OFF;
-#pragma unroll
-      for (int t = 0; t < QT; ++t)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const u32x2 w = lds_read_tr16(sB + bias_rd + (t * 32 + 16 * g + 4 * half) * kDkvBiasRowBytes);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int r = 8 * g + 4 * half + 2 * e;
-              s[t][r] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w[e] & 0xffffu)), kb, s[t][r]);
-              s[t][r + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w[e] >> 16)), kb, s[t][r + 1]);
-            }
-          }
-    }
-    u32x4 pp[QC], ps[QC];
-#pragma unroll
-    for (int t = 0; t < QT; ++t)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int qb = t * 32 + 16 * g + 8 * h;
-        const f32x4 l0 = *(const f32x4*)(&sL[qb]);  // -LSE*log2(e) (unused with PRE)
-        const f32x4 l1 = *(const f32x4*)(&sL[qb + 4]);
-        float pv[8], dsv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p;
-          if constexpr (PRE) {
-            p = fast_exp2(s[t][8 * g + e]);
-          } else {
-            const float nl2 = e < 4 ? l0[e] : l1[e - 4];
-            p = fast_exp2(__builtin_fmaf(s[t][8 * g + e], c, nl2));
-          }
-          if constexpr (MASK) {
-            if (key > q0 + qb + e) p = 0.f;
-          }
-          pv[e] = p;
-          dsv[e] = p * dp[t][8 * g + e];
-        }
-        u32x4 wp, wd;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wp[e] = pack2<BF16>(pv[2 * e], pv[2 * e + 1]);
-          wd[e] = pack2<BF16>(dsv[2 * e], dsv[2 * e + 1]);
-        }
-        pp[2 * t + g] = wp;
-        ps[2 * t + g] = wd;
-      }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (rows: d with perm_o, cols: keys)
-#pragma unroll
-    for (int i = 0; i < DT * QC; ++i) {
-      const int dt = FA_BWD_CHUNK_MAJOR ? i % DT : i / QC;
-      const int qc = FA_BWD_CHUNK_MAJOR ? i / DT : i % QC;
-      const u32x4 ga = tr_operand(sG, to.trl[dt], to.trh[dt], qc, ROWB);
-      const u32x4 qa = tr_operand(sQ, to.trl[dt], to.trh[dt], qc, ROWB);
-      dvt[dt] = mfma32<BF16>(ga, pp[qc], dvt[dt]);
-      pin_step<2, 2, FA_BWD_PIN_LA>(2 * i);
-      dkt[dt] = mfma32<BF16>(qa, ps[qc], dkt[dt]);
-      pin_step<2, 2, FA_BWD_PIN_LA>(2 * i + 1);
-    }
-    pin_tail<2, FA_BWD_PIN_LA>();
-  };
-
-  auto iteration = [&](int qt, char* cur, char* nxt) {
-    if (qt + 1 < n_qt) issue_tile(qt + 1, nxt);
-    const int q0 = qt * BQ;
-    const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
-    if (active) {
-      if (CAUSAL && q0 < kw0 + 31) {
-        tile_body(std::true_type{}, cur, q0);
-      } else {
-        tile_body(std::false_type{}, cur, q0);
-      }
-    }
-    wait_vmem();
-    __syncthreads();
-  };
-
-  char* st0 = smem;
-  char* st1 = smem + STAGE;
-  if (qt_begin < n_qt) issue_tile(qt_begin, st0);
-  wait_vmem();
-  __syncthreads();
-  for (int qt = qt_begin; qt < n_qt; qt += 2) {
-    iteration(qt, st0, st1);
-    if (qt + 1 < n_qt) iteration(qt + 1, st1, st0);
-  }
-
-  // dK = scale dS^T Q, dV: lane (key m, half h) holds d = 32dt + 16h + r.
-  const brsrc_t rdk = make_rsrc(a.dk + base, head_bytes);
-  const brsrc_t rdv = make_rsrc(a.dv + base, head_bytes);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t off = ((uint32_t)key * D + dt * 32 + 16 * h) * 2u;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      u32x4 wk, wv;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wk[t] = pack2<BF16>(dkt[dt][8 * e + 2 * t] * a.scale, dkt[dt][8 * e + 2 * t + 1] * a.scale);
-        wv[t] = pack2<BF16>(dvt[dt][8 * e + 2 * t], dvt[dt][8 * e + 2 * t + 1]);
-      }
-      bstore16(wk, rdk, off + 16 * e, 0);
-      bstore16(wv, rdv, off + 16 * e, 0);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dQ: workgroup owns 128 query rows (32 per wave); loop over 64-key tiles.
-// ---------------------------------------------------------------------------
-constexpr int kDqRows = 128;
-constexpr int kDqBK = 64;
-
-template <int D>
-__host__ __device__ constexpr int dq_stage_bytes() {
-  return 2 * kDqBK * D * 2;  // K, V tiles
-}
-
-template <int D, bool BF16, bool CAUSAL, bool BIAS>
-__global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BK = kDqBK;
-  constexpr int DC = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int KT = BK / 32;
-  constexpr int KC = BK / 16;
-  constexpr int CPR = D / 8;
-  constexpr int ROWB = D * 2;
-  constexpr int LOADS = BK * CPR / kBwdThreads;
-  static_assert(LOADS * kBwdThreads == BK * CPR, "tile split");
-  constexpr int STAGE = dq_stage_bytes<D>();
-  constexpr int TILE = BK * ROWB;
-  // fp16: Q is pre-multiplied by c and the S accumulators start at
-  // -LSE*log2(e) (this lane's row), as in the dK/dV kernel.
-  constexpr bool PRE = FA_BWD_PRESCALE && !BF16;
-
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 31, h = lane >> 5;
-
-  int bh, qt;
-  {
-    const int bid = blockIdx.x;
-    if (CAUSAL) {
-      qt = a.n_tiles - 1 - bid / a.BH;
-      bh = bid % a.BH;
-    } else {
-      const int G = gridDim.x;
-      const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-      bh = lin / a.n_tiles;
-      qt = lin % a.n_tiles;
-    }
-  }
-  const int N = a.N;
-  const size_t base = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const brsrc_t rk = make_rsrc(a.k + base, head_bytes);
-  const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
-  const int qw0 = qt * kDqRows + wave * 32;
-  const int qrow = qw0 + m;
-  const brsrc_t rb =
-      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
-                BIAS ? (uint32_t)N * N * 2 : 0u);
-
-  // Q^T and dO^T as B operands (lane: query m; slot i: d = 16dc + 8h + i).
-  u32x4 qf[DC], gf[DC];
-  {
-    const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
-    const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const uint32_t off = ((uint32_t)qrow * D + dc * 16 + 8 * h) * 2u;
-      qf[dc] = bload16(rq, off, 0);
-      gf[dc] = bload16(rg, off, 0);
-    }
-    if constexpr (PRE) {
-      // Q * c rounded to the input type once: the S MFMAs then yield c*s
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = qf[dc][e];
-          qf[dc][e] = pack2<BF16>(to_f32<BF16>((uint16_t)(w & 0xffffu)) * a.c,
-                                  to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
-        }
-    }
-  }
-  // Rows past N: LSE2 and D read as 0; their Q and dO rows are 0 and dQ is
-  // not stored.
-  float nl2, dl;  // -LSE * log2(e) and -D of this lane's query row
-  {
-    const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
-    const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
-    nl2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
-    dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
-  }
-  const TileOffsets<D> to(lane);
-  uint32_t src[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) src[i] = tile_src_offset<D>(i * kBwdThreads + tid);
-
-  f32x16 dqt[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) dqt[dt] = f32x16{};
-
-  const int kend = CAUSAL ? min(N, qt * kDqRows + kDqRows) : N;
-  const int n_kt = (kend + BK - 1) / BK;
-
-  auto issue_tile = [&](int j, char* stage) {
-    const uint32_t soff = (uint32_t)j * (uint32_t)(BK * ROWB);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int slot = (i * kBwdThreads + wave * 64) * 16;
-      bload16_lds(rk, stage + slot, src[i], soff);
-      bload16_lds(rv, stage + TILE + slot, src[i], soff);
-    }
-  };
-
-  const float c = a.c;
-  auto tile_body = [&](auto mask_tag, const char* stage, int k0) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const char* sK = stage;
-    const char* sV = stage + TILE;
-    // S^T = K Q^T, dP^T - D = V dO^T - D (rows: keys with perm_k, cols:
-    // queries).  Register r of key tile kt holds key kt*32 + 16(r/8) + 8h + r%8.
-    // With a bias, registers 8g..8g+7 of key tile kt need eight consecutive
-    // entries of this lane's bias row: one 16-byte load each, issued first.
-    u32x4 bw[KT][2];
-    if constexpr (BIAS) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-          bw[kt][g] = bload16(rb, ((uint32_t)qrow * (uint32_t)N + (uint32_t)(k0 + 32 * kt + 16 * g + 8 * h)) * 2u, 0);
-    }
-    f32x16 s[KT], dp[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      s[kt] = f32x16{};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dp[kt][r] = dl;  // -D
-        if constexpr (PRE) s[kt][r] = nl2;
-      }
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) {
-        const u32x4 ka = *(const u32x4*)(sK + kt * 32 * ROWB + to.rd[dc]);
-        const u32x4 va = *(const u32x4*)(sV + kt * 32 * ROWB + to.rd[dc]);
-        s[kt] = mfma32<BF16>(ka, qf[dc], s[kt]);
-        pin_step<1, 1, FA_BWD_PIN_LA>(2 * (kt * DC + dc));
-        dp[kt] = mfma32<BF16>(va, gf[dc], dp[kt]);
-        pin_step<1, 1, FA_BWD_PIN_LA>(2 * (kt * DC + dc) + 1);
-      }
-    }
-    pin_tail<1, FA_BWD_PIN_LA>();
-    if constexpr (BIAS) {
-      const float kb = PRE ? kLog2e : 1.0f / a.scale;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = bw[kt][g][e];
-            s[kt][8 * g + 2 * e] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w & 0xffffu)), kb, s[kt][8 * g + 2 * e]);
-            s[kt][8 * g + 2 * e + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w >> 16)), kb, s[kt][8 * g + 2 * e + 1]);
-          }
-    }
-    u32x4 ps[KC];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      float dsv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = PRE ? fast_exp2(s[kt][r]) : fast_exp2(__builtin_fmaf(s[kt][r], c, nl2));
-        if constexpr (MASK) {
-          // causal diagonal; with a bias also keys past N, whose bias entries
-          // are read from the next row and must not reach dS
-          const int keyi = k0 + kt * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-          if ((CAUSAL && keyi > qrow) || (BIAS && keyi >= a.N)) p = 0.f;
-        }
-        dsv[r] = p * dp[kt][r];
-      }
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack2<BF16>(dsv[8 * g + 2 * e], dsv[8 * g + 2 * e + 1]);
-        ps[2 * kt + g] = w;
-      }
-    }
-    // dQ^T += K^T dS^T (rows: d with perm_o, cols: queries)
-#pragma unroll
-    for (int i = 0; i < DT * KC; ++i) {
-      const int dt = FA_BWD_CHUNK_MAJOR ? i % DT : i / KC;
-      const int kc = FA_BWD_CHUNK_MAJOR ? i / DT : i % KC;
-      const u32x4 ka = tr_operand(sK, to.trl[dt], to.trh[dt], kc, ROWB);
-      dqt[dt] = mfma32<BF16>(ka, ps[kc], dqt[dt]);
-      pin_step<2, 2, FA_BWD_PIN_LA>(i);
-    }
-    pin_tail<2, FA_BWD_PIN_LA>();
-  };
-
-  auto iteration = [&](int j, char* cur, char* nxt) {
-    if (j + 1 < n_kt) issue_tile(j + 1, nxt);
-    const int k0 = j * BK;
-    const bool active = !CAUSAL || (k0 <= qw0 + 31);
-    if (active) {
-      if ((CAUSAL && k0 + BK - 1 > qw0) || (BIAS && k0 + BK > a.N)) {
-        tile_body(std::true_type{}, cur, k0);
-      } else {
-        tile_body(std::false_type{}, cur, k0);
-      }
-    }
-    wait_vmem();
-    __syncthreads();
-  };
-
-  char* st0 = smem;
-  char* st1 = smem + STAGE;
-  issue_tile(0, st0);
-  wait_vmem();
-  __syncthreads();
-  for (int j = 0; j < n_kt; j += 2) {
-    iteration(j, st0, st1);
-    if (j + 1 < n_kt) iteration(j + 1, st1, st0);
-  }
-
-  const brsrc_t rdq = make_rsrc(a.dq + base, head_bytes);
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t off = ((uint32_t)qrow * D + dt * 32 + 16 * h) * 2u;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      u32x4 w;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        w[t] = pack2<BF16>(dqt[dt][8 * e + 2 * t] * a.scale, dqt[dt][8 * e + 2 * t + 1] * a.scale);
-      bstore16(w, rdq, off + 16 * e, 0);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// launchers
-// ---------------------------------------------------------------------------
-template <typename Kern>
-static hipError_t set_lds(Kern kern, int bytes) {
-  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
-static BwdArgs make_args(const BwdProblem& p) {
-  BwdArgs a;
-  a.bias = (const uint16_t*)p.bias;
-  a.bias_sb = p.bias_sb;
-  a.bias_sh = p.bias_sh;
-  a.H = p.H;
-  a.q = (const uint16_t*)p.q;
-  a.k = (const uint16_t*)p.k;
-  a.v = (const uint16_t*)p.v;
-  a.dout = (const uint16_t*)p.dout;
-  a.lse2 = p.lse2;
-  a.delta = p.delta;
-  a.dq = (uint16_t*)p.dq;
-  a.dk = (uint16_t*)p.dk;
-  a.dv = (uint16_t*)p.dv;
-  a.N = p.N;
-  a.BH = p.BH;
-  a.c = p.scale * kLog2e;
-  a.scale = p.scale;
-  a.n_tiles = 0;
-  return a;
-}
-
-template <int D, bool BF16, bool O_F32>
-static hipError_t launch_pre_t(const BwdProblem& p, hipStream_t stream) {
-  const int rows = p.BH * p.N;
-  constexpr int RPB = kBwdThreads / (D / 8);
-  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
-  hipLaunchKernelGGL((bwd_pre_kernel<D, BF16, O_F32>), grid, dim3(kBwdThreads), 0, stream, p.o,
-                     (const uint16_t*)p.dout, p.lse, p.delta, p.lse2, rows);
-  return hipGetLastError();
-}
-
-template <int D, bool BF16, bool CAUSAL, bool BIAS>
-static hipError_t launch_dkdv_t(const BwdProblem& p, hipStream_t stream) {
-  BwdArgs a = make_args(p);
-  a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
-  const int lds = 2 * (dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0));
-  auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL, BIAS>;
-  hipError_t e = set_lds(kern, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
-  return hipGetLastError();
-}
-
-template <int D, bool BF16, bool CAUSAL, bool BIAS>
-static hipError_t launch_dq_t(const BwdProblem& p, hipStream_t stream) {
-  BwdArgs a = make_args(p);
-  a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
-  const int lds = 2 * dq_stage_bytes<D>();
-  auto kern = bwd_dq_kernel<D, BF16, CAUSAL, BIAS>;
-  hipError_t e = set_lds(kern, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.BH * a.n_tiles)), dim3(kBwdThreads), lds, stream, a);
-  return hipGetLastError();
-}
-
-// Dispatch over (d, input type) and either the O type (pre) or causal.
-template <template <int, bool, bool> class L>
-static hipError_t dispatch3(const BwdProblem& p, hipStream_t s, bool third) {
-  const bool bf16 = p.dtype == kBF16 || p.dtype == kBF16OutF32;
-  if (p.dtype < kF16 || p.dtype > kBF16OutF32) return hipErrorInvalidValue;
-  if (p.d == 64) {
-    if (bf16) return third ? L<64, true, true>::run(p, s) : L<64, true, false>::run(p, s);
-    return third ? L<64, false, true>::run(p, s) : L<64, false, false>::run(p, s);
-  }
-  if (p.d == 128) {
-    if (bf16) return third ? L<128, true, true>::run(p, s) : L<128, true, false>::run(p, s);
-    return third ? L<128, false, true>::run(p, s) : L<128, false, false>::run(p, s);
-  }
-  return hipErrorInvalidValue;
-}
-template <int D, bool BF16, bool X>
-struct PreL {
-  static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_pre_t<D, BF16, X>(p, s); }
-};
-template <int D, bool BF16, bool X>
-struct DkdvL {
-  static hipError_t run(const BwdProblem& p, hipStream_t s) {
-    return p.bias ? launch_dkdv_t<D, BF16, X, true>(p, s) : launch_dkdv_t<D, BF16, X, false>(p, s);
-  }
-};
-template <int D, bool BF16, bool X>
-struct DqL {
-  static hipError_t run(const BwdProblem& p, hipStream_t s) {
-    return p.bias ? launch_dq_t<D, BF16, X, true>(p, s) : launch_dq_t<D, BF16, X, false>(p, s);
-  }
-};
+#define FA_BWD_DECL(d)                                                   \
+  hipError_t launch_bwd_pre_inst_##d(const BwdProblem&, hipStream_t);  \
+  hipError_t launch_bwd_dkdv_inst_##d(const BwdProblem&, hipStream_t); \
+  hipError_t launch_bwd_dq_inst_##d(const BwdProblem&, hipStream_t);
+FA_BWD_DECL(64)
+FA_BWD_DECL(128)
+FA_BWD_DECL(256)
+#undef FA_BWD_DECL
 
 hipError_t launch_bwd_pre(const BwdProblem& p, hipStream_t s) {
-  return dispatch3<PreL>(p, s, p.dtype == kF16OutF32 || p.dtype == kBF16OutF32);
+  if (p.d == 64) return launch_bwd_pre_inst_64(p, s);
+  if (p.d == 128) return launch_bwd_pre_inst_128(p, s);
+  if (p.d == 256) return launch_bwd_pre_inst_256(p, s);
+  return hipErrorInvalidValue;
 }
-hipError_t launch_bwd_dkdv(const BwdProblem& p, hipStream_t s) { return dispatch3<DkdvL>(p, s, p.causal); }
-hipError_t launch_bwd_dq(const BwdProblem& p, hipStream_t s) { return dispatch3<DqL>(p, s, p.causal); }
+hipError_t launch_bwd_dkdv(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return launch_bwd_dkdv_inst_64(p, s);
+  if (p.d == 128) return launch_bwd_dkdv_inst_128(p, s);
+  if (p.d == 256) return launch_bwd_dkdv_inst_256(p, s);
+  return hipErrorInvalidValue;
+}
+hipError_t launch_bwd_dq(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return launch_bwd_dq_inst_64(p, s);
+  if (p.d == 128) return launch_bwd_dq_inst_128(p, s);
+  if (p.d == 256) return launch_bwd_dq_inst_256(p, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_bwd(const BwdProblem& p, hipStream_t s) {
   hipError_t e = launch_bwd_pre(p, s);

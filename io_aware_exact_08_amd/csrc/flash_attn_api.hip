@@ -13,9 +13,9 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Head dimensions: the forward covers 64, 128 and 256; the backward 64 and 128.
-bool fwd_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
-bool bwd_head_dim(int d) { return d == 64 || d == 128; }
+// Head dimensions: 64, 128 and 256 everywhere except the backward with an
+// attention bias (64 and 128: at d=256 its LDS stages would not fit).
+bool head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
 // The kernels address one head's rows through a buffer resource with a 32-bit
 // byte range and 32-bit offsets, including the rows of a ragged last tile
@@ -29,7 +29,7 @@ bool head_fits_u32(int N, int d, int out_bytes) {
 
 int check_common(int B, int H, int N, int d, float scale, int causal, int dtype, bool fwd) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
-  if (!(fwd ? fwd_head_dim(d) : bwd_head_dim(d))) return FA_ERR_HEADDIM;
+  if (!head_dim(d)) return FA_ERR_HEADDIM;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA_ERR_SHAPE;
   if (dtype < FA_F16 || dtype > FA_BF16_OUT_F32) return FA_ERR_DTYPE;
@@ -100,14 +100,14 @@ int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void*
 }
 
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
-  if (B < 1 || H < 1 || N < 1 || !fwd_head_dim(d)) return 0;
+  if (B < 1 || H < 1 || N < 1 || !head_dim(d)) return 0;
   if (num_splits < 1 || num_splits > 64) return 0;
   return (size_t)num_splits * B * H * N * (d + 1) * sizeof(float);
 }
 
 int flash_attn_fwd_splitkv_default_splits(int B, int H, int N, int d, int causal) {
   (void)causal;
-  if (B < 1 || H < 1 || N < 1 || !fwd_head_dim(d)) return 1;
+  if (B < 1 || H < 1 || N < 1 || !head_dim(d)) return 1;
   // Splitting costs a float32 partial O per split and a merge pass, so it pays
   // only when the unsplit grid leaves compute units idle (at most one
   // workgroup per CU, 256 CUs) over long key ranges: then aim for two
@@ -201,6 +201,7 @@ int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void*
   if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale, causal, dtype, false);
   if (st != FA_OK) return st;
+  if (d == 256) return FA_ERR_HEADDIM;
   if (N > 46340 || bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
@@ -389,7 +390,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_SHAPE:
       return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, (N+256)*d*(output element "
              "bytes) < 2^32 per head, causal 0/1)";
-    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (forward) or 64 or 128 (backward)";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (64 or 128 for the backward with a bias)";
     case FA_ERR_DTYPE: return "unknown dtype code";
     case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -90,7 +90,7 @@ def test_fwd_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dout=None), 1), (dict(dv=None), 1),
-    (dict(N=0), 2), (dict(d=80), 3), (dict(d=256), 3), (dict(dtype=7), 4),
+    (dict(N=0), 2), (dict(d=80), 3), (dict(d=512), 3), (dict(dtype=7), 4),
     (dict(dq=P + 8), 5), (dict(workspace=P + 8), 5),
     (dict(workspace=None), 7), (dict(workspace_bytes=8 * 8 - 1), 7),
     (dict(scale=-1.0), 8),
@@ -123,7 +123,7 @@ def test_product_path_has_no_oracle_or_allocation():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), 1), (dict(workspace=None), 7), (dict(workspace_bytes=10), 7),
-    (dict(d=100), 3), (dict(d=256), 3), (dict(dtype=9), 4), (dict(o=P + 4), 5),
+    (dict(d=100), 3), (dict(d=320), 3), (dict(dtype=9), 4), (dict(o=P + 4), 5),
     (dict(workspace=P + 4), 5),
 ])
 def test_bwd_preprocess_validation(lib, kw, status):
@@ -135,7 +135,7 @@ def test_bwd_preprocess_validation(lib, kw, status):
 
 @pytest.mark.parametrize("stage", ["dkdv", "dq"])
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), 1), (dict(workspace=None), 7), (dict(N=0), 2), (dict(d=16), 3), (dict(d=256), 3),
+    (dict(q=None), 1), (dict(workspace=None), 7), (dict(N=0), 2), (dict(d=16), 3), (dict(d=192), 3),
     (dict(scale=0.0), 8), (dict(causal=3), 2), (dict(k=P + 2), 5),
 ])
 def test_bwd_stage_validation(lib, stage, kw, status):
@@ -254,7 +254,7 @@ def noalloc(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dout=None), 1), (dict(dq=None), 1), (dict(N=0), 2), (dict(N=(1 << 24) - 1, d=128), 2),
-    (dict(d=256), 3), (dict(dtype=8), 4), (dict(dk=P + 8), 5), (dict(scale=0.0), 8),
+    (dict(d=512), 3), (dict(dtype=8), 4), (dict(dk=P + 8), 5), (dict(scale=0.0), 8),
     # the static scratch holds 8 bytes per row: 2^21 rows fit, one more does not
     (dict(B=1, H=32, N=65537), 10), (dict(B=2, H=1, N=(1 << 20) + 1), 10),
 ])

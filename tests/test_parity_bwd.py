@@ -74,7 +74,7 @@ def test_fwd_bwd_workload(causal):
 @pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, False),
                                          (si.FMT_BF16, True)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 300])
 def test_small_shapes(N, d, causal, fmt, out_f32):
     w = si.random_case(1, 2, N, d, fmt, causal, seed=7 * N + d, with_do=True)
@@ -122,6 +122,26 @@ def test_bench_shape_bwd_full():
     """Forward and backward in the benchmark's own launch (B=2 H=12 N=8192 d=64
     fp16 non-causal, the step bench.py times): every element of all 24 heads."""
     w = si.a100_sweep(8192, with_do=True)
+    res = run_fwd_bwd(w)
+    check_heads(w, res)
+
+
+@pytest.mark.parametrize("fmt", [si.FMT_F16, si.FMT_BF16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_bwd(causal, fmt):
+    """d=256 forward and backward (32-row query tiles in dK/dV, 32-key tiles in
+    dQ, accumulators in the accumulation registers) at B=1 H=4 N=1000: 32
+    query tiles of dK/dV, a ragged tail, every element of every head."""
+    w = si.random_case(1, 4, 1000, 256, fmt, causal, seed=2560 + causal, with_do=True)
+    res = run_fwd_bwd(w)
+    check_heads(w, res)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_bwd_bench_shape(causal):
+    """d=256 at B=2 H=8 N=4096 fp16, the benchmarked shape, every element of
+    all 16 heads."""
+    w = si.random_case(2, 8, 4096, 256, si.FMT_F16, causal, seed=2570 + causal, with_do=True)
     res = run_fwd_bwd(w)
     check_heads(w, res)
 
