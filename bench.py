@@ -193,9 +193,8 @@ def config_sweep(fa, si, torch, np, dev):
             ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
                                                  out_f32=out_f32, o=o, lse=lse), reps)
         else:
-            if splits == 0:
-                splits = fa._lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, int(w.causal))
-            ws = torch.empty(fa._lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) // 4,
+            # splits == 0: the library's automatic plan
+            ws = torch.empty(max(fa._lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) // 4, 1),
                              dtype=torch.float32, device=dev)
             ms = timed(lambda: fa.flash_attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale,
                                                          out_f32=out_f32, num_splits=splits,
@@ -204,7 +203,7 @@ def config_sweep(fa, si, torch, np, dev):
                "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                "fwd_frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
         if splits is not None:
-            rec["splits"] = splits
+            rec["splits"] = splits if splits else "automatic"
         if bwd:
             ws = torch.empty(fa.workspace_bytes(B, H, N, d) // 4 + 4, dtype=torch.float32,
                              device=dev)
@@ -219,6 +218,9 @@ def config_sweep(fa, si, torch, np, dev):
 
     for n in (1024, 2048, 4096, 8192):
         run(f"fwd_B2H12N{n}d64_f16", si.a100_sweep(n))
+        # the same through the split-KV entry point's automatic plan (it splits
+        # the key range only where rounds of workgroups would be partly idle)
+        run(f"fwd_splitkv_auto_B2H12N{n}d64_f16", si.a100_sweep(n), splits=0)
     run("fwd_causal_B2H16N4096d128_bf16_spiked_f32out", si.spiked_causal(), out_f32=True)
     run("fwdbwd_causal_B1H8N32768d64_bf16", si.long_causal(with_do=True), bwd=True, reps=3)
     few = si.random_case(1, 4, 8192, 128, "bf16", False, seed=11)
@@ -237,6 +239,8 @@ def config_sweep(fa, si, torch, np, dev):
     for n in (8000, 8200):
         run(f"fwdbwd_B2H12N{n}d64_f16", si.random_case(2, 12, n, 64, "f16", False, seed=n,
                                                         with_do=True), bwd=True)
+        run(f"fwd_splitkv_auto_B2H12N{n}d64_f16", si.random_case(2, 12, n, 64, "f16", False, seed=n),
+            splits=0)
     run("fwdbwd_B2H8N4096d256_f16", si.random_case(2, 8, 4096, 256, "f16", False, seed=257,
                                                      with_do=True), bwd=True)
     run("fwdbwd_causal_B2H8N4096d256_bf16_f32out",

@@ -62,7 +62,7 @@ typedef enum {
   FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */
   FA_ERR_WORKSPACE = 7, /* workspace missing or too small                   */
   FA_ERR_SCALE = 8,     /* scale is not a finite positive number            */
-  FA_ERR_SPLITS = 9,    /* num_splits outside [1, 64]                       */
+  FA_ERR_SPLITS = 9,    /* num_splits outside [0, 64]                       */
   FA_ERR_SCRATCH = 10   /* flash_attn_bwd_noalloc: the problem's workspace
                            exceeds FA_NOALLOC_SCRATCH_BYTES                  */
 } fa_status;
@@ -208,9 +208,17 @@ int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void*
  *   workspace   : device buffer of >= flash_attn_fwd_splitkv_workspace_bytes
  *                 bytes, 16-byte aligned, owned by the caller; contents on
  *                 entry do not matter and on return are unspecified
- *   num_splits  : 1..64 (FA_ERR_SPLITS otherwise); splits beyond the number
- *                 of key tiles are empty and cost one idle workgroup each
- *   Two kernels are enqueued on `stream`.
+ *   num_splits  : 1..64: every query tile's keys split that many ways
+ *                 (splits beyond the number of key tiles are empty and cost
+ *                 one idle workgroup each); 0: an automatic plan for this
+ *                 shape, chosen by a cost model of whole rounds of concurrent
+ *                 workgroups (two per compute unit, one at d=256): no split
+ *                 (then it equals flash_attn_fwd and needs no workspace), a
+ *                 uniform split, or (non-causal) a tail split, in which the
+ *                 query tiles that fill whole rounds run unsplit and write O
+ *                 directly and only the last, partial round's tiles are
+ *                 split; other values give FA_ERR_SPLITS
+ *   Up to three kernels are enqueued on `stream`.
  */
 int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                            void* workspace, size_t workspace_bytes,
@@ -218,7 +226,9 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                            int num_splits, void* stream);
 
 /* Bytes of workspace flash_attn_fwd_splitkv needs: 4 * num_splits * B*H*N*(d+1)
- * (partial O and LSE); 0 for invalid arguments. */
+ * (partial O and LSE); for num_splits = 0 what the automatic plan needs
+ * (the larger of its causal and non-causal plans; 0 when it does not split);
+ * 0 for invalid arguments. */
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 
 /* A split count for this shape, in 1..16: more than 1 only when the unsplit

@@ -126,15 +126,15 @@ def flash_attn_fwd_bias(q, k, v, bias, causal: bool = False, scale=None, out_f32
 def flash_attn_fwd_splitkv(q, k, v, causal: bool = False, scale=None, out_f32: bool = False,
                            num_splits: int = 0, o=None, lse=None, workspace=None):
     """Forward with the key range split over ``num_splits`` workgroups per query
-    tile and merged (0: the library's default for this shape).  Same result
-    as flash_attn_fwd.  The float32 workspace is allocated here unless given."""
+    tile and merged (0: the library's automatic plan for this shape, which may
+    split only the items of the last partial round, or none).  Same result as
+    flash_attn_fwd within rounding.  The float32 workspace is allocated here
+    unless given."""
     torch = _torch()
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check(t, name, (B, H, N, d), q.dtype)
     code = dtype_code(q.dtype, out_f32)
-    if num_splits == 0:
-        num_splits = _lib.flash_attn_fwd_splitkv_default_splits(B, H, N, d, int(bool(causal)))
     odt = torch.float32 if out_f32 else q.dtype
     if o is None:
         o = torch.empty((B, H, N, d), dtype=odt, device=q.device)

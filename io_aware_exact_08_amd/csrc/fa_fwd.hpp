@@ -154,10 +154,15 @@ struct FwdArgs {
   float c;  // scale * log2(e)
   // split-KV: the key tiles of each query tile are cut into `splits` ranges;
   // each workgroup writes its range's O (fp32, normalised by its own sum) and
-  // LSE to part_o [splits][BH][N][D] and part_lse [splits][BH][N].
+  // LSE to part_o [splits][part_rows][D] and part_lse [splits][part_rows],
+  // partial row r holding row part_row_base + r of the flattened [BH*N].
   int splits;
   float* part_o;
   float* part_lse;
+  int part_row_base, part_rows;
+  // non-causal launches cover work items item_base .. item_base + grid/splits
+  // - 1, item i being query tile i % n_qtiles of head i / n_qtiles
+  int item_base;
   // additive attention bias (input type, [N][N] rows per (b, h) at element
   // offset b*bias_sb + h*bias_sh; 0 strides broadcast)
   const uint16_t* bias;
@@ -209,8 +214,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     } else {
       const int G = gridDim.x;
       const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-      bh = lin / (a.n_qtiles * S);
-      qt = (lin / S) % a.n_qtiles;
+      const int item = a.item_base + lin / S;
+      bh = item / a.n_qtiles;
+      qt = item % a.n_qtiles;
       split = lin % S;
     }
   }
@@ -745,12 +751,14 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // A row that saw no key (only possible in a split) has l = 0: O = 0 and
   // LSE = -inf, which the split merge weights by zero.
   if constexpr (SPLITKV) {
-    const size_t pbase = ((size_t)split * a.BH + bh) * (size_t)N;
-    const brsrc_t ro = make_rsrc(a.part_o + pbase * D, (uint32_t)N * D * 4);
-    const brsrc_t rl = make_rsrc(a.part_lse + pbase, (uint32_t)N * 4);
+    // this work item's rows r0 .. r0 + cnt - 1 of the head, as partial rows
+    const int r0 = qt * BQ, cnt = min(BQ, N - r0);
+    const size_t prow = (size_t)split * a.part_rows + (size_t)bh * N + r0 - a.part_row_base;
+    const brsrc_t ro = make_rsrc(a.part_o + prow * D, (uint32_t)cnt * D * 4);
+    const brsrc_t rl = make_rsrc(a.part_lse + prow, (uint32_t)cnt * 4);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int row = qw0 + qb * 32 + m;
+      const int row = qw0 + qb * 32 + m - r0;
       const float lt = sum_halves(l_run[qb]);
       const float ll = BF16 ? sum_halves(l32_run[qb]) : lt;
       const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -856,22 +864,29 @@ hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   a.n_qtiles = (p.N + BQ - 1) / BQ;
   a.c = p.scale * kLog2e;
   a.splits = SPLITKV ? p.splits : 1;
+  a.part_row_base = SPLITKV ? p.part_row_base : 0;
+  a.part_rows = SPLITKV ? (p.part_rows > 0 ? p.part_rows : p.BH * p.N) : 0;
   a.part_o = SPLITKV ? p.part : nullptr;
-  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * p.BH * p.N * D : nullptr;
+  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * a.part_rows * D : nullptr;
+  a.item_base = p.item_base;
+  const int n_items = p.item_count > 0 ? p.item_count : a.BH * a.n_qtiles - p.item_base;
   a.bias = (const uint16_t*)p.bias;
   a.bias_sb = p.bias_sb;
   a.bias_sh = p.bias_sh;
   a.H = p.H;
-  const dim3 grid((unsigned)(a.BH * a.n_qtiles * a.splits));
+  const dim3 grid((unsigned)(n_items * a.splits));
   hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, OUT_F32, SPLITKV, BIAS>), grid, dim3(kThreads), 0,
                      stream, a);
   if (!SPLITKV) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = p.BH * p.N;
+  // merge the partial rows into rows part_row_base .. of O and LSE
+  const int rows = a.part_rows;
   constexpr int RPB = 256 / (D / 4);
+  void* o_rows = (char*)p.o + (size_t)a.part_row_base * D * (OUT_F32 ? 4 : 2);
   hipLaunchKernelGGL((fwd_merge_kernel<D, BF16, OUT_F32>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(256), 0, stream, a.part_o, a.part_lse, p.o, p.lse, rows, p.splits);
+                     dim3(256), 0, stream, a.part_o, a.part_lse, o_rows, p.lse + a.part_row_base, rows,
+                     p.splits);
   return hipGetLastError();
 }
 

@@ -23,6 +23,10 @@ struct FwdProblem {
   int dtype;
   int splits = 1;         // split-KV only: key-range splits
   float* part = nullptr;  // split-KV only: partial O then partial LSE (fp32)
+  int part_row_base = 0;  // split-KV only: first flattened [BH*N] row held in part
+  int part_rows = 0;      // split-KV only: rows held in part (0: all BH*N)
+  int item_base = 0;      // non-causal: first work item (head-major query tiles)
+  int item_count = 0;     // non-causal: work items launched (0: all from item_base)
   int H = 1;              // heads per batch entry (bias addressing)
   const void* bias = nullptr;  // additive attention bias, or null
   long long bias_sb = 0, bias_sh = 0;

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/flash_attn.h"
@@ -39,6 +40,84 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype,
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_SHAPE;
   return FA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Automatic split-KV plan (num_splits = 0)
+// ---------------------------------------------------------------------------
+// A non-causal forward is B*H*ceil(N/BQ) work items of equal length, run by
+// `slots` concurrent workgroups (two per compute unit, one at d=256).  When
+// the items are not a whole number of rounds, the last round leaves compute
+// units idle for a whole item's time (e.g. 768 items on 512 slots take two
+// rounds).  The plan compares, in units of one unsplit item's time:
+//  - no split: ceil(items / slots) rounds;
+//  - every item split S ways along the keys (split-KV): each split item is 1/S
+//    of the work plus a fixed overhead (partial O written in fp32, pipeline
+//    fill) of about four key tiles, plus the merge pass;
+//  - tail split (non-causal): the whole rounds run unsplit and write O
+//    directly, and only the last round's items are split S ways.
+// A split plan must be 3% cheaper than no split.  Causal launches keep the
+// uniform splits of flash_attn_fwd_splitkv_default_splits: their items differ
+// in length and are issued heaviest first.
+struct SplitPlan {
+  int splits = 1;      // key-range splits of the split items
+  int full_items = 0;  // items run unsplit before the split ones (tail split)
+  int row_base = 0;    // first flattened [B*H*N] row of the split items
+};
+
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 256;  // MI355X
+  return cus;
+}
+
+SplitPlan plan_splits(int BH, int N, int d, bool causal) {
+  SplitPlan best;
+  const int bq = fa::fwd_query_tile(d), bk = fa::fwd_key_tile(d);
+  const int n_qt = (N + bq - 1) / bq;
+  const long long items = (long long)BH * n_qt;
+  const int key_tiles = (N + bk - 1) / bk;
+  if (causal) {
+    best.splits = flash_attn_fwd_splitkv_default_splits(1, BH, N, d, 1);
+    return best;
+  }
+  const long long slots = (long long)compute_units() * (d == 256 ? 1 : 2);
+  const double tile = 1.0 / key_tiles, overhead = 4.0 * tile, merge_fixed = 4.0 * tile,
+               merge_rows = 4.0 * tile;
+  auto rounds = [&](long long wgs) { return (double)((wgs + slots - 1) / slots); };
+  double best_cost = rounds(items);
+  const double unsplit = best_cost;
+  const int smax = std::min(16, key_tiles / 4);  // each split keeps at least 4 key tiles
+  for (int S = 2; S <= smax; ++S) {
+    const double c = rounds(items * S) * (1.0 / S + overhead) + merge_fixed + merge_rows;
+    if (c < best_cost && c < 0.97 * unsplit) {
+      best_cost = c;
+      best.splits = S;
+      best.full_items = 0;
+    }
+  }
+  const long long full = (items / slots) * slots, r = items - full;
+  if (full > 0 && r > 0) {
+    for (int S = 2; S <= smax; ++S) {
+      const double c = (double)(full / slots) + rounds(r * S) * (1.0 / S + overhead) + merge_fixed +
+                       merge_rows * (double)r / (double)items;
+      if (c < best_cost && c < 0.97 * unsplit) {
+        best_cost = c;
+        best.splits = S;
+        best.full_items = (int)full;
+      }
+    }
+  }
+  best.row_base = (int)((long long)(best.full_items / n_qt) * N + (long long)(best.full_items % n_qt) * bq);
+  return best;
+}
+
+// Workspace of a plan: float32 partial O and LSE of the split rows, per split.
+size_t plan_workspace_bytes(const SplitPlan& pl, int BH, int N, int d) {
+  if (pl.splits <= 1) return 0;
+  return (size_t)pl.splits * ((size_t)BH * N - (size_t)pl.row_base) * (d + 1) * sizeof(float);
 }
 
 }  // namespace
@@ -101,6 +180,12 @@ int flash_attn_fwd_bias(const void* q, const void* k, const void* v, const void*
 
 size_t flash_attn_fwd_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
   if (B < 1 || H < 1 || N < 1 || !head_dim(d)) return 0;
+  if (num_splits == 0) {
+    // the automatic plan, for either mask
+    const size_t a = plan_workspace_bytes(plan_splits(B * H, N, d, false), B * H, N, d);
+    const size_t c = plan_workspace_bytes(plan_splits(B * H, N, d, true), B * H, N, d);
+    return a > c ? a : c;
+  }
   if (num_splits < 1 || num_splits > 64) return 0;
   return (size_t)num_splits * B * H * N * (d + 1) * sizeof(float);
 }
@@ -129,14 +214,22 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale, causal, dtype, true);
   if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > 64) return FA_ERR_SPLITS;
-  if ((long long)num_splits * B * H * N * (d + 1) >= (1LL << 31)) return FA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 64) return FA_ERR_SPLITS;
+  SplitPlan plan;
+  if (num_splits == 0) {
+    plan = plan_splits(B * H, N, d, causal != 0);
+  } else {
+    plan.splits = num_splits;
+  }
+  if ((long long)plan.splits * B * H * N * (d + 1) >= (1LL << 31)) return FA_ERR_SHAPE;
   if (!head_fits_u32(N, d, 4)) return FA_ERR_SHAPE;  // float32 partial O per split and head
-  if (!workspace || workspace_bytes < flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits))
-    return FA_ERR_WORKSPACE;
-  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  const size_t need = num_splits == 0 ? plan_workspace_bytes(plan, B * H, N, d)
+                                      : flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+  const void* ptrs[] = {q, k, v, o, lse};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
   fa::FwdProblem p;
   p.q = q;
   p.k = k;
@@ -149,8 +242,19 @@ int flash_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   p.scale = scale;
   p.causal = causal != 0;
   p.dtype = dtype;
-  p.splits = num_splits;
+  if (plan.splits <= 1)  // (automatic plan only) nothing to split: the plain forward
+    return fa::launch_fwd(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  if (plan.full_items > 0) {
+    // tail split: the whole rounds first, unsplit, writing O and LSE directly
+    fa::FwdProblem pf = p;
+    pf.item_count = plan.full_items;
+    if (fa::launch_fwd(pf, (hipStream_t)stream) != hipSuccess) return FA_ERR_LAUNCH;
+  }
+  p.splits = plan.splits;
   p.part = (float*)workspace;
+  p.item_base = plan.full_items;
+  p.part_row_base = plan.row_base;
+  p.part_rows = B * H * N - plan.row_base;
   return fa::launch_fwd_splitkv(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -396,7 +500,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_SPLITS: return "num_splits must be between 1 and 64";
+    case FA_ERR_SPLITS: return "num_splits must be between 0 (automatic) and 64";
     case FA_ERR_SCRATCH:
       return "problem too large for the allocation-free entry point's static scratch "
              "(8 * B * H * N bytes must fit FA_NOALLOC_SCRATCH_BYTES)";

@@ -155,7 +155,7 @@ def test_splitkv_workspace_and_default_splits(lib):
     assert lib.flash_attn_fwd_splitkv_workspace_bytes(2, 12, 1024, 64, 3) == 4 * 3 * 24 * 1024 * 65
     assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 1, 8, 128, 1) == 4 * 8 * 129
     assert lib.flash_attn_fwd_splitkv_workspace_bytes(1, 2, 100, 256, 2) == 4 * 2 * 2 * 100 * 257
-    for bad in (dict(num_splits=0), dict(num_splits=65), dict(d=96), dict(d=512), dict(N=0)):
+    for bad in (dict(num_splits=-1), dict(num_splits=65), dict(d=96), dict(d=512), dict(N=0)):
         args = dict(B=1, H=1, N=8, d=64, num_splits=2)
         args.update(bad)
         assert lib.flash_attn_fwd_splitkv_workspace_bytes(**args) == 0
@@ -176,7 +176,7 @@ def test_splitkv_workspace_and_default_splits(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(lse=None), 1), (dict(N=0), 2), (dict(d=80), 3), (dict(dtype=5), 4),
-    (dict(num_splits=0), 9), (dict(num_splits=65), 9), (dict(workspace=None), 7),
+    (dict(num_splits=-1), 9), (dict(num_splits=65), 9), (dict(workspace=None), 7),
     (dict(workspace_bytes=4 * 2 * 8 * 65 - 1), 7), (dict(workspace=P + 4), 5), (dict(o=P + 8), 5),
     (dict(scale=-2.0), 8), (dict(causal=5), 2),
 ])
@@ -268,3 +268,29 @@ def test_noalloc_limit_matches_header(lib):
     text = open(HEADER).read()
     assert "#define FA_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)" in text
     assert lib.NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
+
+
+def test_splitkv_automatic_plan_workspace(lib):
+    """num_splits = 0: the plan's workspace (this container has no GPU, so the
+    plan assumes MI355X's 256 compute units: 512 forward workgroups at once)."""
+    ws = lib.flash_attn_fwd_splitkv_workspace_bytes
+    # whole rounds (1536 items = 3 x 512) and short key ranges: no split
+    assert ws(2, 12, 8192, 64, 0) == 0
+    assert ws(2, 12, 1024, 64, 0) == 0
+    # 768 items = 1.5 rounds: the last 256 items (rows from head 16 on) split in two
+    assert ws(2, 12, 4096, 64, 0) == 2 * (24 * 4096 - 16 * 4096) * 65 * 4
+    # 1560 items: 1536 unsplit, the last 24 (from head 23, tile 41) in 16
+    rows = 24 * 8200 - (23 * 8200 + 41 * 128)
+    assert ws(2, 12, 8200, 64, 0) == 16 * rows * 65 * 4
+    # 256 items on 512 slots: every item split in two
+    assert ws(1, 4, 8192, 128, 0) == 2 * 4 * 8192 * 129 * 4
+
+
+def test_splitkv_automatic_plan_rejects_bad_workspace(lib):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=64, B=2, H=12, N=4096,
+                d=64, scale=0.125, causal=0, dtype=0, num_splits=0, stream=None)
+    assert lib.flash_attn_fwd_splitkv(**args) == 7
+    args.update(workspace=None, workspace_bytes=0)
+    assert lib.flash_attn_fwd_splitkv(**args) == 7
+    args.update(workspace=P + 4, workspace_bytes=1 << 30)
+    assert lib.flash_attn_fwd_splitkv(**args) == 5

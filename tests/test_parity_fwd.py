@@ -338,3 +338,22 @@ def test_bias_hidden_first_tiles_low_logits_f16(kind):
     assert (o20.float() - o0.float()).abs().max().item() <= 2e-3
     assert ((l20 - l0) + 20.0).abs().max().item() <= 1e-3
     assert torch.isfinite(l20).all()
+
+
+@pytest.mark.parametrize("B,H,N,d,fmt,causal,out_f32", [
+    (2, 12, 4096, 64, si.FMT_F16, False, False),   # 1.5 rounds: the last 256 tiles split in two
+    (2, 12, 8200, 64, si.FMT_F16, False, False),   # ragged N: 1536 tiles whole, the last 24 in 16
+    (1, 4, 8192, 128, si.FMT_BF16, False, True),   # half a round: every tile split in two
+    (2, 12, 1024, 64, si.FMT_F16, False, False),   # short key range: no split
+    (2, 12, 4096, 64, si.FMT_F16, True, False),    # causal: the uniform default
+    (1, 3, 3000, 256, si.FMT_BF16, False, True),   # d=256 (one workgroup per compute unit)
+])
+def test_splitkv_automatic_plan(B, H, N, d, fmt, causal, out_f32):
+    """num_splits = 0 (the library's plan) on every element, and within the
+    bound of the plain forward's output."""
+    w = si.random_case(B, H, N, d, fmt, causal, seed=N + d + 7)
+    o, lse = run_splitkv(w, 0, out_f32=out_f32)
+    check(w, o, lse, tag=" automatic splits")
+    o1, l1 = run_fwd(w, out_f32=out_f32)
+    assert (o.float() - o1.float()).abs().max().item() <= TOL_O[fmt]
+    assert (lse - l1).abs().max().item() <= TOL_LSE
