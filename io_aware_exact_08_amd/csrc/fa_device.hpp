@@ -64,6 +64,45 @@ __device__ __forceinline__ void bload16_lds(brsrc_t r, void* lds_base, uint32_t 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
                                            (int)voff, (int)soff, 0, 0);
 }
+// The same direct load written as inline assembly, for pipelines that count
+// every wait themselves.  The compiler does not see it, so it neither holds
+// later LDS reads behind it (it cannot tell which LDS stage a read touches,
+// and would wait for every direct load in flight) nor counts it in its own
+// vmcnt waits: a kernel that uses it must issue no other vector-memory load
+// whose result the compiler waits for while these are in flight.  `rs` is the
+// four-word resource (wave-uniform), `lds` the wave's LDS byte address (form
+// it as an integer from the __shared__ array, not from a generic pointer,
+// which the compiler would keep in a register pair).
+// Nothing is written to registers, so nothing in flight can be overwritten.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+               (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), (uint32_t)kBufferFlags};
+}
+// (m0, which the instruction takes its LDS address from, is restored: the
+// compiler may keep a value of its own there)
+__device__ __forceinline__ void bload16_lds_asm(const u32x4& rs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+// Workgroup barrier for pipelines whose direct loads are counted by hand:
+// this wave's LDS reads have returned (so no stage it read can be refilled
+// under them) and the compiler keeps LDS accesses on their side of it; the
+// caller has already waited (vmcnt) for the loads the other waves will read.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most K vector-memory operations of this wave are outstanding.
 template <int K>

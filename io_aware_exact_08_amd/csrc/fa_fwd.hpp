@@ -41,6 +41,13 @@
 //    2^-11 relative, i.e. < 5e-4 in LSE); the bf16 path keeps a second,
 //    fp32 sum of the unrounded probabilities for the LSE, where a bf16 sum
 //    could be off by 2^-9.
+//  * An attention bias streams from HBM at two bytes per score, so its loads
+//    must be in flight about two key tiles ahead.  The compiler cannot tell
+//    which LDS stage a read touches while a direct load is in flight and
+//    would wait for all of them before each read, so the bias kernels (d <=
+//    128) issue every direct load of the key loop as inline assembly and
+//    count the waits themselves; each wave stages its own bias rows in a
+//    two-tile LDS ring.
 //  * Non-causal launches remap workgroup ids so that all query tiles of a head
 //    run on one XCD (consecutive ids are dealt round-robin over the 8 XCDs),
 //    keeping that head's K/V in one L2.  Causal launches issue the heaviest
@@ -183,8 +190,18 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   constexpr int ROWB = D * 2;  // bytes per K/V row
   constexpr int LOADS = BK * CPR / kThreads;  // 16-byte slots per thread per tile
   static_assert(LOADS * kThreads == BK * CPR, "tile split");
-  constexpr int kStages = FwdCfg<D>::STAGES;
+  // With a bias (d <= 128) each wave streams its bias rows through a ring of
+  // two tiles in LDS, and every direct load of the key loop is issued and
+  // waited for by hand (see the pipeline below).  At d = 64 the K/V pipeline
+  // gives up one stage for the ring, so two workgroups still fit a CU.
+  constexpr bool kBiasLds = BIAS && D <= 128;
+  constexpr int kStages = (kBiasLds && D == 64) ? 3 : FwdCfg<D>::STAGES;
   static_assert(kStages == 3 || kStages == 4, "the pipeline below runs three or four stages");
+  static_assert(!kBiasLds || (QB == 1 && FwdCfg<D>::PREFETCH), "bias ring: one query block, score prefetch");
+  // Pinned operand reads (d = 128) run FA_FWD_PIN_LA MFMAs ahead; with the
+  // bias ring two ahead, which keeps every bias instantiation free of spills
+  // (four ahead spilled 1-9 VGPRs in the causal, bf16 and fp32-output ones).
+  constexpr int kPinLA = kBiasLds ? 2 : FA_FWD_PIN_LA;
   constexpr bool Q_LDS = FwdCfg<D>::Q_LDS;
   static_assert(!Q_LDS || QB == 1, "LDS-resident Q assumes one query block per wave");
   static_assert(!FwdCfg<D>::PIN || QB == 1, "pinned reads count one K read per MFMA");
@@ -193,6 +210,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   __shared__ __attribute__((aligned(16))) uint16_t sV[kStages][BK * D];
   // the workgroup's Q tile, row-major and swizzled like K (Q_LDS only)
   __shared__ __attribute__((aligned(16))) uint16_t sQ[Q_LDS ? BQ * D : 8];
+  // bias ring: wave w, slot t % 2 holds its 32 rows x BK keys of tile t
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kBiasLds ? kWaves * 2 * 32 * BK : 8];
 
   const int tid = threadIdx.x;
   // (wave-uniform for the LDS-resident Q path, which then addresses its DMA
@@ -231,6 +250,19 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   const brsrc_t rb =
       make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
                 BIAS ? (uint32_t)N * N * 2 : 0u);
+  // resource words and LDS addresses of the hand-counted loads (bias ring
+  // only; LDS addresses are formed as 32-bit integers from the arrays
+  // themselves, never through generic pointers)
+  u32x4 wk{}, wv{}, wb{};
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sK[0][0];
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0];
+  const uint32_t lds_b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sB[0];
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (kBiasLds) {
+    wk = rsrc_words(a.k + base, head_bytes);
+    wv = rsrc_words(a.v + base, head_bytes);
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
+  }
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query m, half h), slot i
   // holds d = 16*dc + 8*h + i.  Rows past N read as 0.  With Q_LDS they are
@@ -312,15 +344,55 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     n_kt = (int)(((long long)(split + 1) * total) / a.splits) - j0;
   }
 
-  auto issue_tile = [&](int j, uint16_t* dk, uint16_t* dv) {
-    const uint32_t soff = (uint32_t)(j0 + j) * (uint32_t)(BK * ROWB);
+  // `live` false: a tile past the end, loaded from past the resource (zeros,
+  // no memory traffic) so that the number of loads in flight stays fixed.
+  auto issue_tile = [&](int j, uint16_t* dk, uint16_t* dv, bool live = true) {
+    if constexpr (kBiasLds) {
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(live ? (uint32_t)(j0 + j) * (uint32_t)(BK * ROWB) : head_bytes));
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      char* kb = (char*)dk + (i * kThreads + wave * 64) * 16;
-      char* vb = (char*)dv + (i * kThreads + wave * 64) * 16;
-      bload16_lds(rk, kb, k_gl[i], soff);
-      bload16_lds(rv, vb, v_gl[i], soff);
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t off = (uint32_t)(((dk - &sK[0][0]) * 2) + (i * kThreads + wave_u * 64) * 16);
+        bload16_lds_asm(wk, lds_k + off, k_gl[i], soff);
+        bload16_lds_asm(wv, lds_v + off, v_gl[i], soff);
+      }
+    } else {
+      const uint32_t soff = (uint32_t)(j0 + j) * (uint32_t)(BK * ROWB);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        char* kb = (char*)dk + (i * kThreads + wave * 64) * 16;
+        char* vb = (char*)dv + (i * kThreads + wave * 64) * 16;
+        bload16_lds(rk, kb, k_gl[i], soff);
+        bload16_lds(rv, vb, v_gl[i], soff);
+      }
     }
+  };
+
+  // Bias ring.  A wave's tile block is 32 rows x BK keys, row-major, with the
+  // 16-byte chunks of row r at positions chunk ^ swz_b(r): 16 lanes reading
+  // one chunk of 16 consecutive rows then hit distinct bank slots of the
+  // 256-byte window.  Direct load i, lane l fills slot 64i + l, i.e. row
+  // (64i + l) / CPRB at position (64i + l) % CPRB.
+  constexpr int CPRB = BK / 8;           // 16-byte chunks per bias row of a tile
+  constexpr int RPW = 256 / (BK * 2);    // bias rows per 256-byte window
+  constexpr int LB = 32 * CPRB / 64;     // direct loads per lane per tile
+  auto swz_b = [](int row) { return (row / RPW) % CPRB; };
+  uint32_t b_gl[kBiasLds ? LB : 1];
+  if constexpr (kBiasLds) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / CPRB, pos = p % CPRB;
+      b_gl[i] = (uint32_t)(qw0 + row) * (uint32_t)N * 2u + (uint32_t)((pos ^ swz_b(row)) * 16);
+    }
+  }
+  auto bias_slot = [&](int t) { return sB + (wave * 2 + (t & 1)) * 32 * BK; };
+  auto issue_bias = [&](int t, bool live) {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(live ? (uint32_t)(j0 + t) * (uint32_t)(BK * 2) : (uint32_t)N * (uint32_t)N * 2u));
+    const uint32_t slot = lds_b + (uint32_t)((wave_u * 2 + (t & 1)) * 32 * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) bload16_lds_asm(wb, slot + i * 64 * 16, b_gl[i], soff);
   };
 
   // m_run: exponent reference (log2 units); l_run: sum of the rounded
@@ -338,6 +410,28 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
 
   const float c = a.c;
 
+  // s + bias / scale, so that c * (s + bias/scale) = c*s + bias*log2(e);
+  // applied before the mask, which then overrides whatever the bias read
+  // past the end of a row.  ab[qb][kt][g] holds this lane's bias for keys
+  // 32kt + 16g + 8h + 0..7 of the tile.
+  auto add_bias = [&](f32x16 (&s)[QB][KT], const u32x4 (&ab)[QB][KT][2]) {
+    const float kb = kLog2e / c;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = ab[qb][kt][g][e];
+            s[qb][kt][8 * g + 2 * e] =
+                __builtin_fmaf(to_f32<BF16>((uint16_t)(w & 0xffffu)), kb, s[qb][kt][8 * g + 2 * e]);
+            s[qb][kt][8 * g + 2 * e + 1] =
+                __builtin_fmaf(to_f32<BF16>((uint16_t)(w >> 16)), kb, s[qb][kt][8 * g + 2 * e + 1]);
+          }
+  };
+
   // S^T = K Q^T for one K tile (the scores of 32*KT keys against this wave's
   // query blocks), and with an attention bias its raw bias values: register
   // group g = r/8 of key block kt holds keys k_first + 32kt + 16g + 8h + 0..7,
@@ -349,7 +443,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   auto compute_scores = [&](const uint16_t* Ks, int k_first) {
     const char* Kb = (const char*)Ks;
     Scores sc;
-    if constexpr (BIAS) {
+    if constexpr (BIAS && !kBiasLds) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -376,12 +470,12 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
             pin_step<1, 2, FA_QLDS_LOOKAHEAD>(kt * DC + dc);
           } else {
             sc.v[qb][kt] = mfma32<BF16>(af, qf[qb][dc], sc.v[qb][kt]);
-            if constexpr (FwdCfg<D>::PIN) pin_step<1, 1, FA_FWD_PIN_LA>(kt * DC + dc);
+            if constexpr (FwdCfg<D>::PIN) pin_step<1, 1, kPinLA>(kt * DC + dc);
           }
         }
       }
     if constexpr (Q_LDS) pin_tail<1, FA_QLDS_LOOKAHEAD>();
-    if constexpr (FwdCfg<D>::PIN) pin_tail<1, FA_FWD_PIN_LA>();
+    if constexpr (FwdCfg<D>::PIN) pin_tail<1, kPinLA>();
     return sc;
   };
 
@@ -396,26 +490,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* Vb = (const char*)Vs;
     auto& s = sc.v;
-    if constexpr (BIAS) {
-      // s + bias / scale, so that c * (s + bias/scale) = c*s + bias*log2(e);
-      // applied before the mask, which then overrides whatever the bias read
-      // past the end of a row.
-      const float kb = kLog2e / c;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t w = sc.ab[qb][kt][g][e];
-              s[qb][kt][8 * g + 2 * e] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w & 0xffffu)), kb,
-                                                        s[qb][kt][8 * g + 2 * e]);
-              s[qb][kt][8 * g + 2 * e + 1] = __builtin_fmaf(to_f32<BF16>((uint16_t)(w >> 16)), kb,
-                                                            s[qb][kt][8 * g + 2 * e + 1]);
-            }
-    }
+    if constexpr (BIAS && !kBiasLds) add_bias(s, sc.ab);
+
     // O^T += V^T P^T for packed probabilities pf.
     auto pv = [&](const u32x4 (&pf)[QB][KC]) {
 #pragma unroll
@@ -428,10 +504,10 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
           if constexpr (Q_LDS) pin_step<2, 2, FA_QLDS_LOOKAHEAD>(dt * KC + kc);
-          if constexpr (FwdCfg<D>::PIN) pin_step<2, 2, FA_FWD_PIN_LA>(dt * KC + kc);
+          if constexpr (FwdCfg<D>::PIN) pin_step<2, 2, kPinLA>(dt * KC + kc);
         }
       if constexpr (Q_LDS) pin_tail<2, FA_QLDS_LOOKAHEAD>();
-      if constexpr (FwdCfg<D>::PIN) pin_tail<2, FA_FWD_PIN_LA>();
+      if constexpr (FwdCfg<D>::PIN) pin_tail<2, kPinLA>();
     };
     if constexpr (!BF16) {
       // ---- fp16: lazy reference, overflow detected from the rounded sum ----
@@ -652,10 +728,10 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
           if constexpr (Q_LDS) pin_step<2, 2, FA_QLDS_LOOKAHEAD>(dt * KC + kc);
-          if constexpr (FwdCfg<D>::PIN) pin_step<2, 2, FA_FWD_PIN_LA>(dt * KC + kc);
+          if constexpr (FwdCfg<D>::PIN) pin_step<2, 2, kPinLA>(dt * KC + kc);
         }
       if constexpr (Q_LDS) pin_tail<2, FA_QLDS_LOOKAHEAD>();
-      if constexpr (FwdCfg<D>::PIN) pin_tail<2, FA_FWD_PIN_LA>();
+      if constexpr (FwdCfg<D>::PIN) pin_tail<2, kPinLA>();
     };
     // Causal d <= 128: rows whose max grew are rescaled in a block of their
     // own and the exponentials and P V run on one path.  With two
@@ -693,10 +769,25 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // tile's scores first and the next iteration needs only tile j + 1.
   constexpr bool PREFETCH = FwdCfg<D>::PREFETCH;
   constexpr int kKeep = (PREFETCH ? kStages - 3 : kStages - 2) * kTileLoads;
+  // With the bias ring (kBiasLds) the iteration issues, in this order, tile
+  // j + kAhead's K/V and tile j + 2's bias, both unconditionally (tiles past
+  // the end load nothing), so the loads in flight follow a fixed pattern:
+  //  * tile j's bias was issued after tile j - 2 + kAhead's K/V; newer than
+  //    it when it is read are the K/V of two tiles and one tile's bias;
+  //  * at the end of iteration j tile j + 2's K/V must have landed (the next
+  //    iteration computes its scores); newer than it are kAhead - 2 tiles of
+  //    K/V and kAhead - 1 tiles of bias.
+  // The compiler sees none of these loads, so it adds no waits of its own.
+  constexpr int kBiasKeepRead = 2 * kTileLoads + LB;
+  constexpr int kBiasKeepEnd = (kAhead - 2) * kTileLoads + (kAhead - 1) * LB;
   auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
     constexpr int st = decltype(stage_tag)::value;
-    if (j + kAhead < n_kt)
-      issue_tile(j + kAhead, sK[(st + kAhead) % kStages], sV[(st + kAhead) % kStages]);
+    if constexpr (kBiasLds) {
+      issue_tile(j + kAhead, sK[(st + kAhead) % kStages], sV[(st + kAhead) % kStages], j + kAhead < n_kt);
+    } else {
+      if (j + kAhead < n_kt)
+        issue_tile(j + kAhead, sK[(st + kAhead) % kStages], sV[(st + kAhead) % kStages]);
+    }
     // On the last tile this reads a stale (in-bounds) stage whose scores are
     // never used; keeping it unconditional keeps it in one basic block with
     // the exponentials.
@@ -705,6 +796,21 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     };
     const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + QB * 32 - 1);
+    if constexpr (kBiasLds) {
+      wait_vmem_keep<kBiasKeepRead>();  // this tile's bias has landed
+      if (active) {
+        const char* bb = (const char*)bias_slot(j);
+        u32x4 ab[QB][KT][2];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            ab[0][kt][g] = *(const u32x4*)(bb + m * (BK * 2) + (((4 * kt + 2 * g + h) ^ swz_b(m)) * 16));
+        add_bias(cur.v, ab);
+      }
+      wait_lds();  // (the slot's reads have returned before it is refilled)
+      issue_bias(j + 2, j + 2 < n_kt);
+    }
     if (active) {
       if constexpr (!PREFETCH) cur = compute_scores(sK[st], k0);
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
@@ -716,24 +822,41 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     } else {
       issue_next();
     }
-    if (j + kAhead < n_kt) {
-      wait_vmem_keep<kKeep>();
+    if constexpr (kBiasLds) {
+      wait_vmem_keep<kBiasKeepEnd>();
+      barrier_no_fence();
     } else {
-      wait_vmem();
+      if (j + kAhead < n_kt) {
+        wait_vmem_keep<kKeep>();
+      } else {
+        wait_vmem();
+      }
+      __syncthreads();
     }
-    __syncthreads();
   };
 
   // (with Q_LDS the Q tile's loads were issued first, so they land first)
+  if constexpr (kBiasLds) {
+    // tile 0's bias, K/V of tiles 0 .. kAhead - 1, tile 1's bias: from tile
+    // 1 on, each bias follows the K/V of the tile kAhead - 2 after it, as in
+    // the loop; wait for tiles 0 and 1 (and so for tile 0's bias)
+    issue_bias(0, true);
 #pragma unroll
-  for (int s0 = 0; s0 < kAhead; ++s0)
-    if (s0 < n_kt) issue_tile(s0, sK[s0], sV[s0]);
+    for (int s0 = 0; s0 < kAhead; ++s0) issue_tile(s0, sK[s0], sV[s0], s0 < n_kt);
+    issue_bias(1, 1 < n_kt);
+    wait_vmem_keep<(kAhead - 2) * kTileLoads + LB>();
+    barrier_no_fence();
+  } else {
+#pragma unroll
+    for (int s0 = 0; s0 < kAhead; ++s0)
+      if (s0 < n_kt) issue_tile(s0, sK[s0], sV[s0]);
   if (kAhead < n_kt) {
     wait_vmem_keep<kKeep>();  // tiles 0 and 1 (without the prefetch: tile 0) have landed
   } else {
     wait_vmem();
   }
   __syncthreads();
+  }
   Scores sa, sb;
   if constexpr (PREFETCH) sa = compute_scores(sK[0], j0 * BK);
   for (int j = 0; j < n_kt; j += kStages) {
@@ -746,6 +869,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       sa = sb;  // an odd number of tiles per round: the next round starts from sb
     }
   }
+  // (the ring's loads past the end are still in flight: let them land before
+  // the workgroup's LDS can be handed to another)
+  if constexpr (kBiasLds) wait_vmem();
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
   // A row that saw no key (only possible in a split) has l = 0: O = 0 and

@@ -46,6 +46,22 @@ def test_benchmarked_kernels_do_not_spill(report, name):
     assert r["scratch_bytes_per_lane"] == 0, (name, r)
 
 
+# The d = 64 / 128 bias forwards count their direct loads by hand; the
+# compiler does not see those loads, so it would wait for a spill reload with
+# vmcnt(0) and drain the whole pipeline.  All of them must stay spill-free.
+BIAS_FWD = [f"void fa::fwd_kernel<{d}, {bf}, {c}, {o}, false, true>(fa::FwdArgs)"
+            for d in (64, 128) for bf in ("false", "true") for c in ("false", "true")
+            for o in ("false", "true")]
+
+
+@pytest.mark.parametrize("name", BIAS_FWD)
+def test_bias_forwards_do_not_spill(report, name):
+    r = report["kernels"].get(name)
+    assert r is not None, f"{name} missing from the report"
+    assert r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, (name, r)
+    assert r["scratch_bytes_per_lane"] == 0, (name, r)
+
+
 def test_parser_reads_remarks():
     text = """x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]
 x.hip:1:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]
