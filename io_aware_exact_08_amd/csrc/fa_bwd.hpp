@@ -221,7 +221,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   constexpr int ROWB = D * 2;
   constexpr int LOADS = BQ * CPR / kBwdThreads;
   static_assert(LOADS * kBwdThreads == BQ * CPR, "tile split");
-  constexpr int STAGE = dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0);
+  // With a bias every direct load of the query loop is issued as inline
+  // assembly and waited for by hand, and each wave stages its 32 key columns
+  // of the bias block two query tiles ahead in an LDS ring (see the forward:
+  // the compiler would otherwise wait for all direct loads before each LDS
+  // read).  The ring takes the place of the per-stage bias block.
+  constexpr bool kBiasLds = BIAS && D <= 128;
+  constexpr int STAGE = dkdv_stage_bytes<D>() + ((BIAS && !kBiasLds) ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
   constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
   // fp16: K is pre-multiplied by c = scale*log2(e) and the S accumulators
@@ -272,6 +278,12 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
                       (32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   const int kw0 = kvt * kDkvKeys + wave * 32;  // first key of this wave
   const int key = kw0 + m;                     // this lane's key (column of S)
+  // The same gather from the bias ring, whose rows are this wave's 32 keys
+  // (64 bytes): four rows fill a 256-byte bank window, so the 32 lanes of a
+  // read cycle (rows R..R+3, both column halves) hit every bank slot once.
+  constexpr int kRingRowBytes = 64;
+  const int bias_rd_w = ((lane & 15) >> 2) * kRingRowBytes + 8 * ((lane >> 5) & 1) * kRingRowBytes +
+                        (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
   // K and V as B operands (lane: key m; slot i: d = 16dc + 8h + i).
   u32x4 kf[DC], vf[DC];
@@ -295,6 +307,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
                                   to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
         }
     }
+    if constexpr (kBiasLds) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) {
+        settle(kf[dc]);
+        settle(vf[dc]);
+      }
+    }
   }
   const TileOffsets<D> to(lane);
   uint32_t src[LOADS];
@@ -311,6 +330,39 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   const int n_qt = (N + BQ - 1) / BQ;
   const int qt_begin = CAUSAL ? (kvt * kDkvKeys) / BQ : 0;
 
+  // hand-counted loads (bias only): resource words and 32-bit LDS addresses
+  u32x4 wq{}, wg{}, wl{}, wb{};
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (kBiasLds) {
+    wq = rsrc_words(a.q + base, head_bytes);
+    wg = rsrc_words(a.dout + base, head_bytes);
+    // waves 0, 1 load the LSE2 row, waves 2, 3 the D row (a quarter each)
+    wl = wave_u < 2 ? rsrc_words(a.lse2 + (size_t)bh * N, (uint32_t)N * 4)
+                    : rsrc_words(a.delta + (size_t)bh * N, (uint32_t)N * 4);
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
+  }
+  // `live` false: a tile past the end, read from past the resource (nothing
+  // moves), so that the loads in flight keep a fixed pattern.
+  auto issue_tile_counted = [&](int qt, char* stage, bool live) {
+    const uint32_t st = lds0 + (uint32_t)(stage - smem);
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(live ? (uint32_t)qt * (uint32_t)(BQ * ROWB) : head_bytes));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t slot = (uint32_t)((i * kBwdThreads + wave_u * 64) * 16);
+      bload16_lds_asm(wq, st + slot, src[i], soff);
+      bload16_lds_asm(wg, st + TILE + slot, src[i], soff);
+    }
+    // the BQ LSE2 and BQ D values (2 * BQ * 4 bytes): one load per wave, by
+    // its first BQ / 8 lanes only (a direct load writes every active lane's
+    // slot, zeros past the resource included)
+    const uint32_t lsoff = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(live ? (uint32_t)qt * (uint32_t)(BQ * 4) : (uint32_t)N * 4u));
+    const uint32_t part = (uint32_t)((wave_u & 1) * (BQ * 2));  // byte offset within the row slice
+    if (lane < BQ / 8)
+      bload16_lds_asm(wl, st + 2 * TILE + (wave_u >> 1) * (BQ * 4) + part, part + (uint32_t)(lane * 16), lsoff);
+  };
   auto issue_tile = [&](int qt, char* stage) {
     const uint32_t soff = (uint32_t)qt * (uint32_t)(BQ * ROWB);
 #pragma unroll
@@ -337,8 +389,34 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     }
   };
 
+  // Bias ring: wave w, slot t % 2 holds rows t*BQ .. +63 of its 32 keys
+  // (64 bytes a row); direct load i, lane l fills bytes 16(64i + l), i.e. row
+  // (64i + l) / 4, 16-byte chunk l % 4.  Tile t's bias follows tile t - 1's
+  // Q/dO in issue order (as the loop below issues them), so when it is read
+  // the Q/dO of tiles t and t + 1 and tile t + 1's bias are newer; at the
+  // end of iteration t only tile t + 2's bias is newer than tile t + 1's Q/dO.
+  constexpr int LB = BQ * kRingRowBytes / 16 / 64;  // direct loads per lane per tile
+  constexpr int kTileLoads = 2 * LOADS + 1;
+  const int ring_off = 2 * STAGE;
+  uint32_t b_gl[kBiasLds ? LB : 1];
+  if constexpr (kBiasLds) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int p = i * 64 + lane;
+      b_gl[i] = ((uint32_t)(p / 4) * (uint32_t)N + (uint32_t)(kw0 + (p % 4) * 8)) * 2u;
+    }
+  }
+  auto issue_bias = [&](int t, bool live) {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(live ? (uint32_t)t * (uint32_t)BQ * (uint32_t)N * 2u : (uint32_t)N * (uint32_t)N * 2u));
+    const uint32_t slot = lds0 + (uint32_t)(ring_off + (wave_u * 2 + (t & 1)) * BQ * kRingRowBytes);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) bload16_lds_asm(wb, slot + i * 64 * 16, b_gl[i], soff);
+  };
+
   const float c = a.c;
-  auto tile_body = [&](auto mask_tag, const char* stage, int q0) {
+  // `after_bias`: called once the tile's bias has been read (bias ring only)
+  auto tile_body = [&](auto mask_tag, const char* stage, int q0, auto&& after_bias) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* sQ = stage;
     const char* sG = stage + TILE;
@@ -385,14 +463,27 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e));
       // with PRE the scores are already in log2 units: s + bias*log2(e)
       const float kb = PRE ? kLog2e : 1.0f / a.scale;
-      const char* sB = stage + BIAS_OFF;
+      const char* sB = kBiasLds ? smem + ring_off + (wave * 2 + ((q0 / BQ) & 1)) * BQ * kRingRowBytes
+                                : stage + BIAS_OFF;
+      const int rd0 = kBiasLds ? bias_rd_w : bias_rd;
+      constexpr int pitch = kBiasLds ? kRingRowBytes : kDkvBiasRowBytes;
+      u32x2 bv[QT][2][2];
+      if constexpr (kBiasLds) wait_vmem_keep<2 * kTileLoads + LB>();  // this tile's bias has landed
+#pragma unroll
+      for (int t = 0; t < QT; ++t)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+            bv[t][g][half] = lds_read_tr16(sB + rd0 + (t * 32 + 16 * g + 4 * half) * pitch);
+      after_bias();
 #pragma unroll
       for (int t = 0; t < QT; ++t)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const u32x2 w = lds_read_tr16(sB + bias_rd + (t * 32 + 16 * g + 4 * half) * kDkvBiasRowBytes);
+            const u32x2 w = bv[t][g][half];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               const int r = 8 * g + 4 * half + 2 * e;
@@ -450,29 +541,56 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   };
 
   auto iteration = [&](int qt, char* cur, char* nxt) {
-    if (qt + 1 < n_qt) issue_tile(qt + 1, nxt);
+    if constexpr (kBiasLds) {
+      issue_tile_counted(qt + 1, nxt, qt + 1 < n_qt);
+    } else {
+      if (qt + 1 < n_qt) issue_tile(qt + 1, nxt);
+    }
     const int q0 = qt * BQ;
     const bool active = !CAUSAL || (q0 + BQ - 1 >= kw0);
+    // the ring slot of tile qt is refilled with tile qt + 2's bias as soon as
+    // it has been read (on a skipped tile: right away)
+    auto refill = [&]() {
+      if constexpr (kBiasLds) {
+        wait_lds();
+        issue_bias(qt + 2, qt + 2 < n_qt);
+      }
+    };
     if (active) {
       // d=256: keep each tile's body in its own scheduling region (overlapped
       // with the next one the non-causal kernel spilled ~190 registers)
       if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
       if (CAUSAL && q0 < kw0 + 31) {
-        tile_body(std::true_type{}, cur, q0);
+        tile_body(std::true_type{}, cur, q0, refill);
       } else {
-        tile_body(std::false_type{}, cur, q0);
+        tile_body(std::false_type{}, cur, q0, refill);
       }
       if constexpr (D == 256) __builtin_amdgcn_sched_barrier(0);
+    } else {
+      refill();
     }
-    wait_vmem();
-    __syncthreads();
+    if constexpr (kBiasLds) {
+      wait_vmem_keep<LB>();
+      barrier_no_fence();
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
   };
 
   char* st0 = smem;
   char* st1 = smem + STAGE;
-  if (qt_begin < n_qt) issue_tile(qt_begin, st0);
-  wait_vmem();
-  __syncthreads();
+  if constexpr (kBiasLds) {
+    issue_bias(qt_begin, qt_begin < n_qt);
+    issue_tile_counted(qt_begin, st0, qt_begin < n_qt);
+    issue_bias(qt_begin + 1, qt_begin + 1 < n_qt);
+    wait_vmem_keep<LB>();  // tile qt_begin's Q/dO (and so its bias)
+    barrier_no_fence();
+  } else {
+    if (qt_begin < n_qt) issue_tile(qt_begin, st0);
+    wait_vmem();
+    __syncthreads();
+  }
   if constexpr (D == 256) {
     // one tile body per loop trip, stages swapped at run time (unrolled by
     // two, the non-causal kernel spilled ~190 registers)
@@ -488,6 +606,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       if (qt + 1 < n_qt) iteration(qt + 1, st1, st0);
     }
   }
+  if constexpr (kBiasLds) wait_vmem();  // (the ring's loads past the end)
 
   // dK = scale dS^T Q, dV: lane (key m, half h) holds d = 32dt + 16h + r.
   const brsrc_t rdk = make_rsrc(a.dk + base, head_bytes);
@@ -522,6 +641,12 @@ template <int D>
 __host__ __device__ constexpr int dq_stage_bytes() {
   return 2 * dq_bk<D>() * D * 2;  // K, V tiles
 }
+// With a bias each wave stages its 32 rows of two key tiles' bias in LDS
+// (see bwd_dq_kernel), behind the two K/V stages.
+template <int D, bool BIAS>
+__host__ __device__ constexpr int dq_ring_bytes() {
+  return BIAS ? (kBwdThreads / 64) * 2 * 32 * dq_bk<D>() * 2 : 0;
+}
 
 template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel(BwdArgs a) {
@@ -539,6 +664,11 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   // fp16: Q is pre-multiplied by c and the S accumulators start at
   // -LSE*log2(e) (this lane's row), as in the dK/dV kernel.
   constexpr bool PRE = FA_BWD_PRESCALE && !BF16;
+  // With a bias every direct load of the key loop is issued as inline
+  // assembly and waited for by hand, and each wave stages its bias rows two
+  // key tiles ahead in an LDS ring (the forward's scheme: the compiler would
+  // otherwise wait for all direct loads before each LDS read).
+  constexpr bool kBiasLds = BIAS && D <= 128;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -601,6 +731,15 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     nl2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
     dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
   }
+  if constexpr (kBiasLds) {
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      settle(qf[dc]);
+      settle(gf[dc]);
+    }
+    settle(nl2);
+    settle(dl);
+  }
   const TileOffsets<D> to(lane);
   uint32_t src[LOADS];
 #pragma unroll
@@ -613,18 +752,76 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   const int kend = CAUSAL ? min(N, qt * kDqRows + kDqRows) : N;
   const int n_kt = (kend + BK - 1) / BK;
 
-  auto issue_tile = [&](int j, char* stage) {
-    const uint32_t soff = (uint32_t)j * (uint32_t)(BK * ROWB);
+  // hand-counted loads (bias only): resource words and 32-bit LDS addresses
+  u32x4 wk{}, wv{}, wb{};
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (kBiasLds) {
+    wk = rsrc_words(a.k + base, head_bytes);
+    wv = rsrc_words(a.v + base, head_bytes);
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
+  }
+  // `live` false: a tile past the end, read from past the resource (nothing
+  // moves), so that the loads in flight keep a fixed pattern.
+  auto issue_tile = [&](int j, char* stage, bool live = true) {
+    if constexpr (kBiasLds) {
+      const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(live ? (uint32_t)j * (uint32_t)(BK * ROWB) : head_bytes));
+      const uint32_t st = lds0 + (uint32_t)(stage - smem);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int slot = (i * kBwdThreads + wave * 64) * 16;
-      bload16_lds(rk, stage + slot, src[i], soff);
-      bload16_lds(rv, stage + TILE + slot, src[i], soff);
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t slot = (uint32_t)((i * kBwdThreads + wave_u * 64) * 16);
+        bload16_lds_asm(wk, st + slot, src[i], soff);
+        bload16_lds_asm(wv, st + TILE + slot, src[i], soff);
+      }
+    } else {
+      const uint32_t soff = (uint32_t)j * (uint32_t)(BK * ROWB);
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int slot = (i * kBwdThreads + wave * 64) * 16;
+        bload16_lds(rk, stage + slot, src[i], soff);
+        bload16_lds(rv, stage + TILE + slot, src[i], soff);
+      }
     }
   };
 
+  // Bias ring (the forward's layout): wave w, slot t % 2 holds its 32 rows x
+  // BK keys of tile t, row-major, 16-byte chunk c of row r at position
+  // c ^ swz_b(r); direct load i, lane l fills slot position 64i + l.
+  constexpr int CPRB = BK / 8;
+  constexpr int RPW = 256 / (BK * 2);
+  constexpr int LB = 32 * CPRB / 64;  // direct loads per lane per tile
+  auto swz_b = [](int row) { return (row / RPW) % CPRB; };
+  const int ring_off = 2 * STAGE;
+  uint32_t b_gl[kBiasLds ? LB : 1];
+  if constexpr (kBiasLds) {
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / CPRB, pos = p % CPRB;
+      b_gl[i] = (uint32_t)(qw0 + row) * (uint32_t)N * 2u + (uint32_t)((pos ^ swz_b(row)) * 16);
+    }
+  }
+  auto issue_bias = [&](int t, bool live) {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(live ? (uint32_t)t * (uint32_t)(BK * 2) : (uint32_t)N * (uint32_t)N * 2u));
+    const uint32_t slot = lds0 + (uint32_t)(ring_off + (wave_u * 2 + (t & 1)) * 32 * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) bload16_lds_asm(wb, slot + i * 64 * 16, b_gl[i], soff);
+  };
+
   const float c = a.c;
-  auto tile_body = [&](auto mask_tag, const char* stage, int k0) {
+  // this lane's bias for keys 32kt + 16g + 8h + 0..7 of a tile, read from the
+  // ring
+  auto read_bias = [&](int j, u32x4 (&bw)[KT][2]) {
+    const char* bb = smem + ring_off + (wave * 2 + (j & 1)) * 32 * BK * 2;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        bw[kt][g] = *(const u32x4*)(bb + m * (BK * 2) + (((4 * kt + 2 * g + h) ^ swz_b(m)) * 16));
+  };
+  auto tile_body = [&](auto mask_tag, const char* stage, int k0, const u32x4 (&bw_ring)[KT][2]) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* sK = stage;
     const char* sV = stage + TILE;
@@ -633,7 +830,12 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     // With a bias, registers 8g..8g+7 of key tile kt need eight consecutive
     // entries of this lane's bias row: one 16-byte load each, issued first.
     u32x4 bw[KT][2];
-    if constexpr (BIAS) {
+    if constexpr (kBiasLds) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) bw[kt][g] = bw_ring[kt][g];
+    } else if constexpr (BIAS) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -708,30 +910,60 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     pin_tail<2, FA_BWD_PIN_LA>();
   };
 
+  // Bias ring load order: tile t's bias follows tile t - 1's K/V, so when
+  // tile j's bias is read, the K/V of tiles j and j + 1 and tile j + 1's bias
+  // are newer; at the end of iteration j only tile j + 2's bias is newer than
+  // tile j + 1's K/V.
+  constexpr int kTileLoads = 2 * LOADS;
   auto iteration = [&](int j, char* cur, char* nxt) {
-    if (j + 1 < n_kt) issue_tile(j + 1, nxt);
+    if constexpr (kBiasLds) {
+      issue_tile(j + 1, nxt, j + 1 < n_kt);
+      wait_vmem_keep<2 * kTileLoads + LB>();  // tile j's bias has landed
+    } else {
+      if (j + 1 < n_kt) issue_tile(j + 1, nxt);
+    }
     const int k0 = j * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 31);
+    u32x4 bw[KT][2];
+    if constexpr (kBiasLds) {
+      if (active) read_bias(j, bw);
+      wait_lds();  // (the slot's reads have returned before it is refilled)
+      issue_bias(j + 2, j + 2 < n_kt);
+    }
     if (active) {
       if ((CAUSAL && k0 + BK - 1 > qw0) || (BIAS && k0 + BK > a.N)) {
-        tile_body(std::true_type{}, cur, k0);
+        tile_body(std::true_type{}, cur, k0, bw);
       } else {
-        tile_body(std::false_type{}, cur, k0);
+        tile_body(std::false_type{}, cur, k0, bw);
       }
     }
-    wait_vmem();
-    __syncthreads();
+    if constexpr (kBiasLds) {
+      wait_vmem_keep<LB>();
+      barrier_no_fence();
+    } else {
+      wait_vmem();
+      __syncthreads();
+    }
   };
 
   char* st0 = smem;
   char* st1 = smem + STAGE;
-  issue_tile(0, st0);
-  wait_vmem();
-  __syncthreads();
+  if constexpr (kBiasLds) {
+    issue_bias(0, true);
+    issue_tile(0, st0);
+    issue_bias(1, 1 < n_kt);
+    wait_vmem_keep<LB>();  // tile 0's K/V (and so tile 0's bias)
+    barrier_no_fence();
+  } else {
+    issue_tile(0, st0);
+    wait_vmem();
+    __syncthreads();
+  }
   for (int j = 0; j < n_kt; j += 2) {
     iteration(j, st0, st1);
     if (j + 1 < n_kt) iteration(j + 1, st1, st0);
   }
+  if constexpr (kBiasLds) wait_vmem();  // (the ring's loads past the end)
 
   const brsrc_t rdq = make_rsrc(a.dq + base, head_bytes);
 #pragma unroll
@@ -805,7 +1037,7 @@ template <int D, bool BF16, bool CAUSAL, bool BIAS>
 hipError_t launch_dq_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
-  const int lds = 2 * dq_stage_bytes<D>();
+  const int lds = 2 * dq_stage_bytes<D>() + dq_ring_bytes<D, BIAS>();
   auto kern = bwd_dq_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;

@@ -102,6 +102,12 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Make the compiler wait here for a value it loaded (an empty asm that reads
+// it).  Kernels with hand-counted loads call it on their compiler-visible
+// loads before the loop: left to the first use inside the loop, the
+// compiler's wait would count none of the hand-counted loads and drain them.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) { asm volatile("" ::"v"(v)); }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most K vector-memory operations of this wave are outstanding.
