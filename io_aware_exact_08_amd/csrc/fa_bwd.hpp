@@ -182,6 +182,14 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 // second half's exponentials can run under those MFMAs.  Measured on MI355X
 // against d-tile outermost: causal dK/dV -1.7% (B2 H12 N4096 fp16), dQ -1.5%
 // (B1 H8 N32768 bf16 causal) and -0.5% (B2 H12 N8192 fp16), others unchanged.
+// Hand-counted direct loads for the unbiased kernels (the bias kernels always
+// count theirs).  Same-box A/B against the compiler's waits: d=128 non-causal
+// dQ -9.8% and dK/dV -1.1% (B2 H12 N4096 fp16), so those use them; at d=64
+// the headline shape moved within +-1.5%, causal N=4096 dQ +2.6%, B1 H8
+// N32768 bf16 causal dQ -2.9%, d=128 bf16 causal dQ +1.9%, dK/dV -2.1%.
+#ifndef FA_BWD_COUNTED
+#define FA_BWD_COUNTED 0
+#endif
 #ifndef FA_BWD_PRESCALE
 #define FA_BWD_PRESCALE 1
 #endif
@@ -226,7 +234,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   // of the bias block two query tiles ahead in an LDS ring (see the forward:
   // the compiler would otherwise wait for all direct loads before each LDS
   // read).  The ring takes the place of the per-stage bias block.
-  constexpr bool kBiasLds = BIAS && D <= 128;
+  constexpr bool kCounted = D <= 128 && (BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL));
+  constexpr bool kBiasLds = BIAS && kCounted;
   constexpr int STAGE = dkdv_stage_bytes<D>() + ((BIAS && !kBiasLds) ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
   constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
@@ -307,7 +316,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
                                   to_f32<BF16>((uint16_t)(w >> 16)) * a.c);
         }
     }
-    if constexpr (kBiasLds) {
+    if constexpr (kCounted) {
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         settle(kf[dc]);
@@ -334,14 +343,15 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   u32x4 wq{}, wg{}, wl{}, wb{};
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if constexpr (kBiasLds) {
+  if constexpr (kCounted) {
     wq = rsrc_words(a.q + base, head_bytes);
     wg = rsrc_words(a.dout + base, head_bytes);
     // waves 0, 1 load the LSE2 row, waves 2, 3 the D row (a quarter each)
     wl = wave_u < 2 ? rsrc_words(a.lse2 + (size_t)bh * N, (uint32_t)N * 4)
                     : rsrc_words(a.delta + (size_t)bh * N, (uint32_t)N * 4);
-    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
   }
+  if constexpr (kBiasLds)
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
   // `live` false: a tile past the end, read from past the resource (nothing
   // moves), so that the loads in flight keep a fixed pattern.
   auto issue_tile_counted = [&](int qt, char* stage, bool live) {
@@ -543,6 +553,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   auto iteration = [&](int qt, char* cur, char* nxt) {
     if constexpr (kBiasLds) {
       issue_tile_counted(qt + 1, nxt, qt + 1 < n_qt);
+    } else if constexpr (kCounted) {
+      if (qt + 1 < n_qt) issue_tile_counted(qt + 1, nxt, true);
     } else {
       if (qt + 1 < n_qt) issue_tile(qt + 1, nxt);
     }
@@ -572,6 +584,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
     if constexpr (kBiasLds) {
       wait_vmem_keep<LB>();
       barrier_no_fence();
+    } else if constexpr (kCounted) {
+      wait_vmem();
+      barrier_no_fence();
     } else {
       wait_vmem();
       __syncthreads();
@@ -580,7 +595,11 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
 
   char* st0 = smem;
   char* st1 = smem + STAGE;
-  if constexpr (kBiasLds) {
+  if constexpr (kCounted && !kBiasLds) {
+    if (qt_begin < n_qt) issue_tile_counted(qt_begin, st0, true);
+    wait_vmem();
+    barrier_no_fence();
+  } else if constexpr (kBiasLds) {
     issue_bias(qt_begin, qt_begin < n_qt);
     issue_tile_counted(qt_begin, st0, qt_begin < n_qt);
     issue_bias(qt_begin + 1, qt_begin + 1 < n_qt);
@@ -668,7 +687,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   // assembly and waited for by hand, and each wave stages its bias rows two
   // key tiles ahead in an LDS ring (the forward's scheme: the compiler would
   // otherwise wait for all direct loads before each LDS read).
-  constexpr bool kBiasLds = BIAS && D <= 128;
+  constexpr bool kCounted = D <= 128 && (BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL));
+  constexpr bool kBiasLds = BIAS && kCounted;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -731,7 +751,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     nl2 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, qrow * 4, 0, 0));
     dl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, qrow * 4, 0, 0));
   }
-  if constexpr (kBiasLds) {
+  if constexpr (kCounted) {
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       settle(qf[dc]);
@@ -756,15 +776,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   u32x4 wk{}, wv{}, wb{};
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)smem;
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if constexpr (kBiasLds) {
+  if constexpr (kCounted) {
     wk = rsrc_words(a.k + base, head_bytes);
     wv = rsrc_words(a.v + base, head_bytes);
-    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
   }
+  if constexpr (kBiasLds)
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
   // `live` false: a tile past the end, read from past the resource (nothing
   // moves), so that the loads in flight keep a fixed pattern.
   auto issue_tile = [&](int j, char* stage, bool live = true) {
-    if constexpr (kBiasLds) {
+    if constexpr (kCounted) {
       const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
           (int)(live ? (uint32_t)j * (uint32_t)(BK * ROWB) : head_bytes));
       const uint32_t st = lds0 + (uint32_t)(stage - smem);
@@ -940,6 +961,9 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     if constexpr (kBiasLds) {
       wait_vmem_keep<LB>();
       barrier_no_fence();
+    } else if constexpr (kCounted) {
+      wait_vmem();
+      barrier_no_fence();
     } else {
       wait_vmem();
       __syncthreads();
@@ -957,7 +981,11 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   } else {
     issue_tile(0, st0);
     wait_vmem();
-    __syncthreads();
+    if constexpr (kCounted) {
+      barrier_no_fence();
+    } else {
+      __syncthreads();
+    }
   }
   for (int j = 0; j < n_kt; j += 2) {
     iteration(j, st0, st1);

@@ -76,6 +76,14 @@ namespace fa {
 #ifndef FA_FWD_MIN_WAVES
 #define FA_FWD_MIN_WAVES 2
 #endif
+// Hand-counted direct loads for the unbiased d <= 128 forwards too (the
+// compiler's own waits drained the next tile's loads before the first K read
+// of every iteration).  Same-box A/B, bit-identical: B2 H12 N8192 d64 fp16
+// -1.3 to -3.8%, bf16 -0.8%, d128 B2 H12 N4096 fp16 -7.7% and bf16 -4%; the
+// fp16 causal d=64 kernel measured +0.9 to +1.5% and keeps the compiler's.
+#ifndef FA_FWD_COUNTED
+#define FA_FWD_COUNTED 1
+#endif
 #ifndef FA_FWD256_PREFETCH
 #define FA_FWD256_PREFETCH 0
 #endif
@@ -194,14 +202,16 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // two tiles in LDS, and every direct load of the key loop is issued and
   // waited for by hand (see the pipeline below).  At d = 64 the K/V pipeline
   // gives up one stage for the ring, so two workgroups still fit a CU.
-  constexpr bool kBiasLds = BIAS && D <= 128;
+  constexpr bool kCounted =
+      D <= 128 && (BIAS || (FA_FWD_COUNTED && !SPLITKV && !(D == 64 && CAUSAL && !BF16)));
+  constexpr bool kBiasLds = BIAS && kCounted;
   constexpr int kStages = (kBiasLds && D == 64) ? 3 : FwdCfg<D>::STAGES;
   static_assert(kStages == 3 || kStages == 4, "the pipeline below runs three or four stages");
   static_assert(!kBiasLds || (QB == 1 && FwdCfg<D>::PREFETCH), "bias ring: one query block, score prefetch");
   // Pinned operand reads (d = 128) run FA_FWD_PIN_LA MFMAs ahead; with the
   // bias ring two ahead, which keeps every bias instantiation free of spills
   // (four ahead spilled 1-9 VGPRs in the causal, bf16 and fp32-output ones).
-  constexpr int kPinLA = kBiasLds ? 2 : FA_FWD_PIN_LA;
+  constexpr int kPinLA = kCounted ? 2 : FA_FWD_PIN_LA;
   constexpr bool Q_LDS = FwdCfg<D>::Q_LDS;
   static_assert(!Q_LDS || QB == 1, "LDS-resident Q assumes one query block per wave");
   static_assert(!FwdCfg<D>::PIN || QB == 1, "pinned reads count one K read per MFMA");
@@ -258,11 +268,12 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0];
   const uint32_t lds_b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sB[0];
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if constexpr (kBiasLds) {
+  if constexpr (kCounted) {
     wk = rsrc_words(a.k + base, head_bytes);
     wv = rsrc_words(a.v + base, head_bytes);
-    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
   }
+  if constexpr (kBiasLds)
+    wb = rsrc_words(a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh, (uint32_t)N * N * 2);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane (query m, half h), slot i
   // holds d = 16*dc + 8*h + i.  Rows past N read as 0.  With Q_LDS they are
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // `live` false: a tile past the end, loaded from past the resource (zeros,
   // no memory traffic) so that the number of loads in flight stays fixed.
   auto issue_tile = [&](int j, uint16_t* dk, uint16_t* dv, bool live = true) {
-    if constexpr (kBiasLds) {
+    if constexpr (kCounted) {
       const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(
           (int)(live ? (uint32_t)(j0 + j) * (uint32_t)(BK * ROWB) : head_bytes));
 #pragma unroll
@@ -778,8 +789,9 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   //    iteration computes its scores); newer than it are kAhead - 2 tiles of
   //    K/V and kAhead - 1 tiles of bias.
   // The compiler sees none of these loads, so it adds no waits of its own.
-  constexpr int kBiasKeepRead = 2 * kTileLoads + LB;
-  constexpr int kBiasKeepEnd = (kAhead - 2) * kTileLoads + (kAhead - 1) * LB;
+  constexpr int LBc = kBiasLds ? LB : 0;  // bias loads per tile in the count
+  constexpr int kBiasKeepRead = 2 * kTileLoads + LBc;
+  constexpr int kCountedKeepEnd = (kAhead - 2) * kTileLoads + (kAhead - 1) * LBc;
   auto iteration = [&](int j, auto stage_tag, Scores& cur, Scores& nxt) {
     constexpr int st = decltype(stage_tag)::value;
     if constexpr (kBiasLds) {
@@ -823,15 +835,21 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       issue_next();
     }
     if constexpr (kBiasLds) {
-      wait_vmem_keep<kBiasKeepEnd>();
+      wait_vmem_keep<kCountedKeepEnd>();
       barrier_no_fence();
     } else {
+      // (without a bias no load is issued past the end, so the last kAhead
+      // iterations wait for everything)
       if (j + kAhead < n_kt) {
         wait_vmem_keep<kKeep>();
       } else {
         wait_vmem();
       }
-      __syncthreads();
+      if constexpr (kCounted) {
+        barrier_no_fence();
+      } else {
+        __syncthreads();
+      }
     }
   };
 
