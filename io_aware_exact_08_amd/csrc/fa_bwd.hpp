@@ -187,6 +187,11 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 // dQ -9.8% and dK/dV -1.1% (B2 H12 N4096 fp16), so those use them; at d=64
 // the headline shape moved within +-1.5%, causal N=4096 dQ +2.6%, B1 H8
 // N32768 bf16 causal dQ -2.9%, d=128 bf16 causal dQ +1.9%, dK/dV -2.1%.
+// d=256 (one wave per SIMD): counted loads measured dQ -7% (B2 H8 N4096
+// fp16), -6.5% (bf16), -11% (bf16 causal); dK/dV within 0.5%, -2.2% causal.
+#ifndef FA_BWD256_COUNTED
+#define FA_BWD256_COUNTED 1
+#endif
 #ifndef FA_BWD_COUNTED
 #define FA_BWD_COUNTED 0
 #endif
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   // of the bias block two query tiles ahead in an LDS ring (see the forward:
   // the compiler would otherwise wait for all direct loads before each LDS
   // read).  The ring takes the place of the per-stage bias block.
-  constexpr bool kCounted = D <= 128 && (BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL));
+  constexpr bool kCounted = BIAS ? D <= 128
+                                 : (FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED));
   constexpr bool kBiasLds = BIAS && kCounted;
   constexpr int STAGE = dkdv_stage_bytes<D>() + ((BIAS && !kBiasLds) ? kDkvBiasBytes : 0);
   constexpr int TILE = BQ * ROWB;
@@ -687,7 +693,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   // assembly and waited for by hand, and each wave stages its bias rows two
   // key tiles ahead in an LDS ring (the forward's scheme: the compiler would
   // otherwise wait for all direct loads before each LDS read).
-  constexpr bool kCounted = D <= 128 && (BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL));
+  constexpr bool kCounted = BIAS ? D <= 128
+                                 : (FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED));
   constexpr bool kBiasLds = BIAS && kCounted;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
