@@ -1,0 +1,376 @@
+// Fused exact-attention forward for head dimension 256 on 16x16x32 MFMAs.
+//
+// The method is fwd_kernel's (page 2 of the subject, "Kernel Fusion" and
+// "Tiling": scores, online softmax and P V per tile, one normalisation at the
+// end, O and the row LSE written once).  What changes is the mapping, chosen
+// so that two waves fit each SIMD at d = 256:
+//  * A workgroup is 8 waves (two per SIMD) of 16 query rows each, 128 rows in
+//    all.  A wave's O^T (256 d x 16 queries) is 16 accumulator tiles of four
+//    registers, 64 in all, and its Q^T operand 32 registers; with 32 queries
+//    per wave (fwd_kernel) O alone takes 128 and the accumulators had to be
+//    parked in the accumulation registers around every product.
+//  * S^T = K Q^T per 16-key block with v_mfma_f32_16x16x32: lane l holds
+//    query l%16 and keys 4(l/16) .. 4(l/16)+3 of the block.  A row's 32 keys
+//    of a tile sit in lanes l%16 + 16g, g = 0..3, so its max and sum combine
+//    over those four lanes (ds_swizzle for the xor-16 pair, permlane32_swap
+//    for the halves).  Every O register of a lane belongs to its query, so a
+//    rescale multiplies the lane's 64 accumulators by one factor, and the row
+//    max is cheap enough to take on every tile (one exponential/P V path for
+//    both input types).
+//  * The lane's eight probabilities of a tile (keys 4g+j and 16+4g+j, j < 4)
+//    are exactly the eight k-slots it supplies to O^T += V^T P^T; the V^T
+//    operand is read with ds_read_b64_tr_b16 from the same two groups of four
+//    keys, so P goes from the score registers to the next product directly.
+//  * K and V tiles of 32 keys stream through four LDS stages (128 KB) by
+//    direct buffer->LDS loads that the kernel counts itself (the compiler would
+//    otherwise wait for all of them before every LDS read).  K rows are
+//    swizzled so that the 16 lanes reading one chunk of 16 consecutive rows
+//    hit 16 bank slots; V rows so that the transposing read's 32 lanes of a
+//    cycle (8 rows x 2 chunks) do.
+#pragma once
+
+#include "fa_fwd.hpp"
+
+namespace fa {
+
+// C[16x16] += A[16x32] * B[32x16], fp32 accumulate.  Lane l supplies row
+// (l%16) of A and column (l%16) of B, eight k-values each (k = 8(l/16) + i);
+// lane l receives column l%16, rows 4(l/16) .. 4(l/16)+3.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// The value of lane l ^ 16 (ds_swizzle in bit mode: and 0x1f, or 0, xor 0x10,
+// within each 32-lane half).
+__device__ __forceinline__ float swap16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+}
+// Max and sum over lanes l, l^16, l^32, l^48 (identical in all four).
+__device__ __forceinline__ float max4(float x) { return max_halves(fmaxf(x, swap16(x))); }
+__device__ __forceinline__ float sum4(float x) { return sum_halves(x + swap16(x)); }
+
+__device__ __forceinline__ void bstore8(u32x2 v, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
+}
+
+constexpr int kW256 = 8;              // waves per workgroup (two per SIMD)
+constexpr int kT256 = kW256 * 64;     // threads
+constexpr int kBQ256 = kW256 * 16;    // query rows per workgroup
+constexpr int kBK256 = 32;            // keys per tile
+constexpr int kSt256 = 4;             // LDS stages
+static_assert(kBQ256 == kWaves * FwdCfg<256>::QB * 32, "query tile seen by the split plan");
+
+#ifndef FA_FWD256W_LA
+#define FA_FWD256W_LA 4
+#endif
+
+template <bool BF16, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
+  constexpr int D = 256;
+  constexpr int ROWB = D * 2;                     // bytes per K/V row
+  constexpr int BK = kBK256, BQ = kBQ256;
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int LOADS = BK * CPR / kT256;         // direct loads per thread per tensor
+  static_assert(LOADS * kT256 == BK * CPR, "tile split");
+  constexpr int kTileLoads = 2 * LOADS;           // per thread per tile (K and V)
+  constexpr int kAhead = kSt256 - 1;              // prefetch distance in tiles
+  constexpr int STAGEB = BK * ROWB;               // bytes per stage and tensor
+  constexpr int LA = FA_FWD256W_LA;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kSt256][BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kSt256][BK * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15;  // this lane's query within the wave's 16 rows
+  const int g = lane >> 4;  // its quarter of the wave
+
+  int bh, qt;
+  {
+    const int bid = blockIdx.x;
+    if (CAUSAL) {
+      qt = a.n_qtiles - 1 - bid / a.BH;  // heaviest query tiles first
+      bh = bid % a.BH;
+    } else {
+      // a head's query tiles on one XCD (ids are dealt round-robin over 8)
+      const int G = gridDim.x;
+      const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+      const int item = a.item_base + lin;
+      bh = item / a.n_qtiles;
+      qt = item % a.n_qtiles;
+    }
+  }
+  const int N = a.N;
+  const size_t base = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const int qw0 = qt * BQ + wave * 16;  // first query row of this wave
+  const int qrow = qw0 + m;
+
+  // Q^T operand (B of S^T = K Q^T): register group dc holds d = 32dc + 8g ..
+  // +7 of this lane's query row (rows past N read as 0).  Settled before the
+  // loop, whose loads the compiler does not see.
+  u32x4 qf[8];
+  {
+    const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) qf[dc] = bload16(rq, ((uint32_t)qrow * D + 32 * dc + 8 * g) * 2u, 0);
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) settle(qf[dc]);
+  }
+
+  // K operand (A): key m of a 16-key block, chunk 4dc + g, stored at chunk
+  // position (4dc + g) ^ (row & 15) (the XOR stays in the chunk's 256-byte
+  // window, so offsets repeat every four dc).
+  int kr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kr[i] = m * ROWB + (((4 * i + g) ^ m) * 16);
+  auto k_off = [&](int dc) { return kr[dc & 3] + (dc >> 2) * 256; };
+  // V^T operand (A of O^T += V^T P^T) through the transposing read: in
+  // quarter g, lane 4j + q reads key 4g + j (16 + 4g + j for k-slots 4..7) at
+  // d = 16dt + 4q .. +3, i.e. chunk 2dt + q/2 at position
+  // (2dt + q/2) ^ 2(key & 7), bytes (q & 1) * 8; lane i then receives
+  // d = 16dt + i for those four keys.
+  int vr[8];
+  {
+    const int j = m >> 2, q = m & 3, key = 4 * g + j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      vr[i] = key * ROWB + (((2 * i + (q >> 1)) ^ ((key & 7) << 1)) * 16) + (q & 1) * 8;
+  }
+  auto v_off = [&](int dt) { return vr[dt & 7] + (dt >> 3) * 256; };
+
+  // Direct-load slots: thread slot p = i * kT256 + tid holds tile row p / CPR
+  // at chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
+  uint32_t k_gl[LOADS], v_gl[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = i * kT256 + tid;
+    const int row = p / CPR, pos = p % CPR;
+    k_gl[i] = (uint32_t)(row * ROWB + ((pos ^ (row & 15)) * 16));
+    v_gl[i] = (uint32_t)(row * ROWB + ((pos ^ ((row & 7) << 1)) * 16));
+  }
+  const u32x4 wk = rsrc_words(a.k + base, head_bytes);
+  const u32x4 wv = rsrc_words(a.v + base, head_bytes);
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sK[0][0];
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0];
+  auto issue_tile = [&](int j, int st) {
+    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)j * (uint32_t)STAGEB));
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const uint32_t slot = (uint32_t)(st * STAGEB + (i * kT256 + wave * 64) * 16);
+      bload16_lds_asm(wk, lds_k + slot, k_gl[i], soff);
+      bload16_lds_asm(wv, lds_v + slot, v_gl[i], soff);
+    }
+  };
+
+  const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
+  const int n_kt = (kend + BK - 1) / BK;
+  const float c = a.c;
+
+  // m_run: exponent reference (log2 units, the row's); l_run: this lane's
+  // share of the sum of the rounded probabilities; l32_run: its fp32 sum (bf16
+  // LSE).
+  float m_run = -INFINITY, l_run = 0.f, l32_run = 0.f;
+  f32x4 oacc[16];
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // S^T of one K tile: s[kb][r] is key 16kb + 4g + r of the tile.
+  struct S2 {
+    f32x4 v[2];
+  };
+  auto scores = [&](const char* Kb) {
+    S2 s;
+    s.v[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s.v[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+        const u32x4 ka = *(const u32x4*)(Kb + kb * 16 * ROWB + k_off(dc));
+        s.v[kb] = mfma16<BF16>(ka, qf[dc], s.v[kb]);
+        pin_step<1, 1, LA>(kb * 8 + dc);
+      }
+    pin_tail<1, LA>();
+    return s;
+  };
+  // O^T += V^T P^T for the packed probabilities pf (k-slot i: key
+  // 4g + i for i < 4, 16 + 4g + i - 4 after).
+  auto pv = [&](const char* Vb, const u32x4& pf) {
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const u32x2 lo = lds_read_tr16(Vb + v_off(dt));
+      const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + 16 * ROWB);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      oacc[dt] = mfma16<BF16>(vf, pf, oacc[dt]);
+      pin_step<2, 2, LA>(dt);
+    }
+    pin_tail<2, LA>();
+  };
+  // p = 2^(c*s + neg_m) rounded to the input type and packed as the P^T
+  // operand; ts: sum of the rounded values, ts32: their fp32 sum.
+  auto exp_pack = [&](const S2& s, float neg_m, u32x4& pf, float& ts, float& ts32) {
+    float p[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[4 * kb + r] = fast_exp2(__builtin_fmaf(s.v[kb][r], c, neg_m));
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pf[e] = pack2<BF16>(p[2 * e], p[2 * e + 1]);
+      if (e & 1) t1 = sum2<BF16>(pf[e], t1); else t0 = sum2<BF16>(pf[e], t0);
+    }
+    ts = t0 + t1;
+    if constexpr (BF16) ts32 = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  };
+  auto row_max = [&](const S2& s) {
+    const float a0 = fmaxf(fmaxf(s.v[0][0], s.v[0][1]), fmaxf(s.v[0][2], s.v[0][3]));
+    const float a1 = fmaxf(fmaxf(s.v[1][0], s.v[1][1]), fmaxf(s.v[1][2], s.v[1][3]));
+    return max4(fmaxf(a0, a1));
+  };
+
+  // Online softmax of one tile and its P V.  MASK: the causal diagonal and
+  // the end of the sequence.
+  auto softmax_pv = [&](auto mask_tag, S2& s, const char* Vb, int k0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
+      const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 16 * kb + 4 * g + r > lim) s.v[kb][r] = -INFINITY;
+    }
+    u32x4 pf;
+    float ts = 0.f, ts32 = 0.f;
+    // The row max costs eight compares and two exchanges here, so both types
+    // take it on every tile: bf16 keeps the exact running max (the dominant
+    // probability is then exactly 1), fp16 moves its reference only when the
+    // max rises more than 8 (log2 units) above it, which keeps every
+    // probability at most 2^8.  Rows that do not move keep alpha = 1 exactly.
+    const float mnew = row_max(s) * c;
+    const bool grow = mnew > m_run + rescale_threshold<BF16>();
+    if (__ballot(grow) != 0ull) {
+      const float mn = grow ? mnew : m_run;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+      l32_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) oacc[dt] *= alpha;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+    exp_pack(s, neg_m, pf, ts, ts32);
+    l_run += ts;
+    l32_run += ts32;
+    pv(Vb, pf);
+  };
+
+  // Pipeline: iteration j (tile j in stage j % 4) starts tile j + 3's loads,
+  // computes tile j's scores, softmax and P V, and before the barrier waits
+  // until tile j + 1 has landed: all but the newest two tiles' loads (all of
+  // them once no load was started).
+  auto iteration = [&](int j, auto stage_tag) {
+    constexpr int st = decltype(stage_tag)::value;
+    if (j + kAhead < n_kt) issue_tile(j + kAhead, (st + kAhead) % kSt256);
+    const int k0 = j * BK;
+    const bool active = !CAUSAL || (k0 <= qw0 + 15);
+    if (active) {
+      S2 s = scores((const char*)sK[st]);
+      const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
+      if (need_mask) {
+        softmax_pv(std::true_type{}, s, (const char*)sV[st], k0);
+      } else {
+        softmax_pv(std::false_type{}, s, (const char*)sV[st], k0);
+      }
+    }
+    if (j + kAhead < n_kt) {
+      wait_vmem_keep<(kSt256 - 2) * kTileLoads>();
+    } else {
+      wait_vmem();
+    }
+    barrier_no_fence();
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < kAhead; ++s0)
+    if (s0 < n_kt) issue_tile(s0, s0);
+  if (kAhead < n_kt) {
+    wait_vmem_keep<(kSt256 - 2) * kTileLoads>();  // tile 0 has landed
+  } else {
+    wait_vmem();
+  }
+  barrier_no_fence();
+  for (int j = 0; j < n_kt; j += kSt256) {
+    iteration(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < n_kt) iteration(j + 2, std::integral_constant<int, 2>{});
+    if (j + 3 < n_kt) iteration(j + 3, std::integral_constant<int, 3>{});
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+  // Lane (query m, quarter g) holds d = 16dt + 4g .. +3 of its row; rows past
+  // N are dropped by the stores.
+  const brsrc_t ro = make_rsrc((const char*)a.o + base * (OUT_F32 ? 4 : 2), (uint32_t)N * D * (OUT_F32 ? 4 : 2));
+  const brsrc_t rl = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const float lt = sum4(l_run);
+  const float ll = BF16 ? sum4(l32_run) : lt;
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) {
+    const uint32_t col = (uint32_t)(16 * dt + 4 * g);
+    if constexpr (OUT_F32) {
+      u32x4 w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = __float_as_uint(oacc[dt][t] * inv);
+      bstore16(w, ro, ((uint32_t)qrow * D + col) * 4u, 0);
+    } else {
+      const u32x2 w = {pack2<BF16>(oacc[dt][0] * inv, oacc[dt][1] * inv),
+                       pack2<BF16>(oacc[dt][2] * inv, oacc[dt][3] * inv)};
+      bstore8(w, ro, ((uint32_t)qrow * D + col) * 2u, 0);
+    }
+  }
+  if (g == 0) bstore4((m_run + fast_log2(ll)) * kLn2, rl, (uint32_t)qrow * 4u, 0);
+}
+
+template <bool BF16, bool CAUSAL, bool OUT_F32>
+hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
+  FwdArgs a{};
+  a.q = (const uint16_t*)p.q;
+  a.k = (const uint16_t*)p.k;
+  a.v = (const uint16_t*)p.v;
+  a.o = p.o;
+  a.lse = p.lse;
+  a.N = p.N;
+  a.BH = p.BH;
+  a.n_qtiles = (p.N + kBQ256 - 1) / kBQ256;
+  a.c = p.scale * kLog2e;
+  a.splits = 1;
+  a.item_base = CAUSAL ? 0 : p.item_base;
+  const int n_items = p.item_count > 0 ? p.item_count : a.BH * a.n_qtiles - a.item_base;
+  hipLaunchKernelGGL((fwd256_kernel<BF16, CAUSAL, OUT_F32>), dim3((unsigned)n_items), dim3(kT256), 0, stream, a);
+  return hipGetLastError();
+}
+
+inline hipError_t launch_fwd256(const FwdProblem& p, hipStream_t s) {
+  const bool bf16 = p.dtype == kBF16 || p.dtype == kBF16OutF32;
+  const bool f32 = p.dtype == kF16OutF32 || p.dtype == kBF16OutF32;
+  if (p.dtype < kF16 || p.dtype > kBF16OutF32) return hipErrorInvalidValue;
+  if (bf16) {
+    if (f32) return p.causal ? launch_fwd256_t<true, true, true>(p, s) : launch_fwd256_t<true, false, true>(p, s);
+    return p.causal ? launch_fwd256_t<true, true, false>(p, s) : launch_fwd256_t<true, false, false>(p, s);
+  }
+  if (f32) return p.causal ? launch_fwd256_t<false, true, true>(p, s) : launch_fwd256_t<false, false, true>(p, s);
+  return p.causal ? launch_fwd256_t<false, true, false>(p, s) : launch_fwd256_t<false, false, false>(p, s);
+}
+
+}  // namespace fa

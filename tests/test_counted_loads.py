@@ -1,11 +1,12 @@
-"""The bias kernels (d = 64, 128) issue the direct loads of their key or
-query loop as inline assembly and count the waits themselves.  The compiler
-does not see those loads, so any vmcnt wait it inserted inside the loop would
-miscount them (and a vmcnt(0) would drain the whole pipeline).  Compile the
-d = 64 forward and backward slices to assembly and check that no
-compiler-inserted vmcnt wait appears at or after the first loop header of any
-bias kernel.  Waits written in the sources sit between the assembler's
-inline-asm markers and are skipped."""
+"""The bias kernels (d = 64, 128) and the d = 256 forward issue the direct
+loads of their key or query loop as inline assembly and count the waits
+themselves.  The compiler does not see those loads, so any vmcnt wait it
+inserted inside the loop would miscount them (and a vmcnt(0) would drain the
+whole pipeline).  Compile the d = 64 forward and backward slices and the
+d = 256 forward slice to assembly and check that no compiler-inserted vmcnt
+wait appears at or after the first loop header of any such kernel.  Waits
+written in the sources sit between the assembler's inline-asm markers and are
+skipped."""
 import os
 import re
 import subprocess
@@ -15,13 +16,14 @@ import pytest
 from io_aware_exact_08_amd import build
 
 BIAS_KERNEL = re.compile(r"^(_ZN2fa\d+(?:fwd_kernel|bwd_dkdv_kernel|bwd_dq_kernel)I\S*ELb1EEEvNS_7[FB]wdArgsE):")
+FWD256_KERNEL = re.compile(r"^(_ZN2fa13fwd256_kernelI\S*EEvNS_7FwdArgsE):")
 
 
-def compiler_waits_in_loop(asm_text):
+def compiler_waits_in_loop(asm_text, kernel=BIAS_KERNEL):
     """{kernel: [compiler-inserted vmcnt waits at or after its first loop header]}."""
     out, cur, in_loop, in_asm = {}, None, False, False
     for line in asm_text.splitlines():
-        m = BIAS_KERNEL.match(line)
+        m = kernel.match(line)
         if m:
             cur, in_loop, in_asm = m.group(1), False, False
             out[cur] = []
@@ -56,20 +58,23 @@ def test_detector_on_a_sample():
         "_ZN2fa13bwd_dq_kernelILi64ELb0ELb0ELb1EEEvNS_7BwdArgsE": ["s_waitcnt vmcnt(1) lgkmcnt(0)"]}
 
 
-@pytest.mark.parametrize("src,extra", [("fa_fwd_inst.hip", ["-DFA_INST_KIND=1"]), ("fa_bwd_inst.hip", [])])
-def test_bias_loops_have_no_compiler_vmcnt_waits(tmp_path, src, extra):
+@pytest.mark.parametrize("src,extra,kernel", [
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=64", "-DFA_INST_KIND=1"], BIAS_KERNEL),
+    ("fa_bwd_inst.hip", ["-DFA_INST_D=64"], BIAS_KERNEL),
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=0"], FWD256_KERNEL)])
+def test_counted_loops_have_no_compiler_vmcnt_waits(tmp_path, src, extra, kernel):
     try:
         hipcc = build.hipcc()
     except RuntimeError:
         pytest.skip("hipcc is not installed")
     out = str(tmp_path / "k.s")
-    cmd = [hipcc] + build.HIPCC_FLAGS + ["-DFA_INST_D=64"] + extra + [
+    cmd = [hipcc] + build.HIPCC_FLAGS + extra + [
         "-I", os.path.join(build.ROOT, "include"), "--cuda-device-only", "-S",
         os.path.join(build.CSRC, src), "-o", out]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     with open(out) as f:
-        found = compiler_waits_in_loop(f.read())
+        found = compiler_waits_in_loop(f.read(), kernel)
     assert len(found) >= 8, sorted(found)
     bad = {k: v for k, v in found.items() if v}
     assert not bad, bad

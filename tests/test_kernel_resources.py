@@ -62,6 +62,20 @@ def test_bias_forwards_do_not_spill(report, name):
     assert r["scratch_bytes_per_lane"] == 0, (name, r)
 
 
+# The d = 256 forward counts its K/V loads the same way.
+FWD256 = [f"void fa::fwd256_kernel<{bf}, {c}, {o}>(fa::FwdArgs)"
+          for bf in ("false", "true") for c in ("false", "true") for o in ("false", "true")]
+
+
+@pytest.mark.parametrize("name", FWD256)
+def test_d256_forwards_do_not_spill(report, name):
+    r = report["kernels"].get(name)
+    assert r is not None, f"{name} missing from the report"
+    assert r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, (name, r)
+    assert r["scratch_bytes_per_lane"] == 0, (name, r)
+    assert r["occupancy_waves_per_simd"] >= 2, (name, r)  # two waves per SIMD by design
+
+
 def test_parser_reads_remarks():
     text = """x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]
 x.hip:1:1: remark:     VGPRs: 128 [-Rpass-analysis=kernel-resource-usage]
