@@ -238,9 +238,16 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
     return max4(fmaxf(a0, a1));
   };
 
-  // Online softmax of one tile and its P V.  MASK: the causal diagonal and
-  // the end of the sequence.
-  auto softmax_pv = [&](auto mask_tag, S2& s, const char* Vb, int k0) {
+  // Online softmax of one tile up to its packed probabilities.  MASK: the
+  // causal diagonal and the end of the sequence.  The row max costs eight
+  // compares and two exchanges here, so both types take it on every tile:
+  // bf16 keeps the exact running max (the dominant probability is then
+  // exactly 1), fp16 moves its reference only when the max rises more than 8
+  // (log2 units) above it, which keeps every probability at most 2^8.  Rows
+  // that do not move get alpha = 1 exactly.  The exponentials use the new
+  // reference, so only the rescale of O (below) depends on whether a row
+  // moved.
+  auto softmax = [&](auto mask_tag, S2& s, int k0, u32x4& pf, float& alpha, bool& grow) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
       const int lim = CAUSAL ? min(qrow, N - 1) : N - 1;  // last visible key
@@ -250,51 +257,56 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
         for (int r = 0; r < 4; ++r)
           if (k0 + 16 * kb + 4 * g + r > lim) s.v[kb][r] = -INFINITY;
     }
-    u32x4 pf;
-    float ts = 0.f, ts32 = 0.f;
-    // The row max costs eight compares and two exchanges here, so both types
-    // take it on every tile: bf16 keeps the exact running max (the dominant
-    // probability is then exactly 1), fp16 moves its reference only when the
-    // max rises more than 8 (log2 units) above it, which keeps every
-    // probability at most 2^8.  Rows that do not move keep alpha = 1 exactly.
     const float mnew = row_max(s) * c;
-    const bool grow = mnew > m_run + rescale_threshold<BF16>();
+    grow = mnew > m_run + rescale_threshold<BF16>();
+    const float mn = grow ? mnew : m_run;
+    alpha = grow ? ((m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mn)) : 1.0f;
+    m_run = mn;
+    float ts, ts32 = 0.f;
+    exp_pack(s, (mn == -INFINITY) ? 0.f : -mn, pf, ts, ts32);
+    l_run = __builtin_fmaf(l_run, alpha, ts);
+    if constexpr (BF16) l32_run = __builtin_fmaf(l32_run, alpha, ts32);
+  };
+  auto rescale_pv = [&](const char* Vb, const u32x4& pf, float alpha, bool grow) {
     if (__ballot(grow) != 0ull) {
-      const float mn = grow ? mnew : m_run;
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
-      l32_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) oacc[dt] *= alpha;
     }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    exp_pack(s, neg_m, pf, ts, ts32);
-    l_run += ts;
-    l32_run += ts32;
     pv(Vb, pf);
   };
 
   // Pipeline: iteration j (tile j in stage j % 4) starts tile j + 3's loads,
-  // computes tile j's scores, softmax and P V, and before the barrier waits
-  // until tile j + 1 has landed: all but the newest two tiles' loads (all of
-  // them once no load was started).
+  // computes tile j + 1's scores alongside tile j's softmax (the MFMAs of the
+  // one cover the exponentials of the other), then tile j's P V, and before
+  // the barrier waits until tile j + 2 has landed: all but the newest tile's
+  // loads (all of them once no load was started).  Past the last tile the
+  // score read lands on a stage that is not being written and its result is
+  // dropped.
+  S2 s_cur;
   auto iteration = [&](int j, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
+    constexpr int st1 = (st + 1) % kSt256;
     if (j + kAhead < n_kt) issue_tile(j + kAhead, (st + kAhead) % kSt256);
     const int k0 = j * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 15);
     if (active) {
-      S2 s = scores((const char*)sK[st]);
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
+      u32x4 pf;
+      float alpha;
+      bool grow;
+      S2 s_next;
       if (need_mask) {
-        softmax_pv(std::true_type{}, s, (const char*)sV[st], k0);
+        s_next = scores((const char*)sK[st1]);
+        softmax(std::true_type{}, s_cur, k0, pf, alpha, grow);
       } else {
-        softmax_pv(std::false_type{}, s, (const char*)sV[st], k0);
+        s_next = scores((const char*)sK[st1]);
+        softmax(std::false_type{}, s_cur, k0, pf, alpha, grow);
       }
+      rescale_pv((const char*)sV[st], pf, alpha, grow);
+      s_cur = s_next;
     }
     if (j + kAhead < n_kt) {
-      wait_vmem_keep<(kSt256 - 2) * kTileLoads>();
+      wait_vmem_keep<(kSt256 - 3) * kTileLoads>();
     } else {
       wait_vmem();
     }
@@ -305,11 +317,12 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   for (int s0 = 0; s0 < kAhead; ++s0)
     if (s0 < n_kt) issue_tile(s0, s0);
   if (kAhead < n_kt) {
-    wait_vmem_keep<(kSt256 - 2) * kTileLoads>();  // tile 0 has landed
+    wait_vmem_keep<(kSt256 - 3) * kTileLoads>();  // tiles 0 and 1 have landed
   } else {
     wait_vmem();
   }
   barrier_no_fence();
+  s_cur = scores((const char*)sK[0]);
   for (int j = 0; j < n_kt; j += kSt256) {
     iteration(j, std::integral_constant<int, 0>{});
     if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{});
