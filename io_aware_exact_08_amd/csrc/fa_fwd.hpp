@@ -88,10 +88,8 @@ namespace fa {
 // next tile's loads before the first LDS read of each iteration was fully
 // exposed: counted loads measured -16% (B2 H8 N4096 fp16), -14% (bf16) and
 // -12% (bf16 causal, fp32 O), bit-identical.
-// Plain (unbiased, unsplit) d=256 forwards run fwd256_kernel (fa_fwd256.hpp).
-#ifndef FA_FWD256_WIDE
-#define FA_FWD256_WIDE 1
-#endif
+// Unbiased d=256 forwards (plain and split-KV) run fwd256_kernel
+// (fa_fwd256.hpp); fwd_kernel<256> serves the biased one.
 #ifndef FA_FWD256_COUNTED
 #define FA_FWD256_COUNTED 1
 #endif

@@ -71,7 +71,10 @@ static_assert(kBQ256 == kWaves * FwdCfg<256>::QB * 32, "query tile seen by the s
 #define FA_FWD256W_LA 4
 #endif
 
-template <bool BF16, bool CAUSAL, bool OUT_F32>
+// SPLITKV: the key tiles of each query tile are cut into a.splits ranges and
+// each workgroup writes its range's O (fp32, normalised by its own sum) and
+// LSE as partial rows, which fwd_merge_kernel combines (OUT_F32 unused).
+template <bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
 __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   constexpr int D = 256;
   constexpr int ROWB = D * 2;                     // bytes per K/V row
@@ -93,19 +96,23 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   const int m = lane & 15;  // this lane's query within the wave's 16 rows
   const int g = lane >> 4;  // its quarter of the wave
 
-  int bh, qt;
+  int bh, qt, split = 0;
   {
     const int bid = blockIdx.x;
+    const int S = SPLITKV ? a.splits : 1;
     if (CAUSAL) {
-      qt = a.n_qtiles - 1 - bid / a.BH;  // heaviest query tiles first
-      bh = bid % a.BH;
+      qt = a.n_qtiles - 1 - bid / (a.BH * S);  // heaviest query tiles first
+      const int rem = bid % (a.BH * S);
+      bh = rem / S;
+      split = rem % S;
     } else {
       // a head's query tiles on one XCD (ids are dealt round-robin over 8)
       const int G = gridDim.x;
       const int lin = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-      const int item = a.item_base + lin;
+      const int item = a.item_base + lin / S;
       bh = item / a.n_qtiles;
       qt = item % a.n_qtiles;
+      split = lin % S;
     }
   }
   const int N = a.N;
@@ -161,8 +168,19 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   const u32x4 wv = rsrc_words(a.v + base, head_bytes);
   const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sK[0][0];
   const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0];
+  const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
+  // This workgroup's key tiles: j0 .. j0 + n_kt - 1 (all of them unless split;
+  // a split may hold none).
+  int j0 = 0, n_kt = (kend + BK - 1) / BK;
+  if constexpr (SPLITKV) {
+    const int total = n_kt;
+    j0 = (int)(((long long)split * total) / a.splits);
+    n_kt = (int)(((long long)(split + 1) * total) / a.splits) - j0;
+  }
+  // local tile j (global tile j0 + j) into stage st
   auto issue_tile = [&](int j, int st) {
-    const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)j * (uint32_t)STAGEB));
+    const uint32_t soff =
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 + j) * (uint32_t)STAGEB));
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const uint32_t slot = (uint32_t)(st * STAGEB + (i * kT256 + wave * 64) * 16);
@@ -171,8 +189,6 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
     }
   };
 
-  const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
-  const int n_kt = (kend + BK - 1) / BK;
   const float c = a.c;
 
   // m_run: exponent reference (log2 units, the row's); l_run: this lane's
@@ -287,7 +303,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
     constexpr int st = decltype(stage_tag)::value;
     constexpr int st1 = (st + 1) % kSt256;
     if (j + kAhead < n_kt) issue_tile(j + kAhead, (st + kAhead) % kSt256);
-    const int k0 = j * BK;
+    const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 15);
     if (active) {
       const bool need_mask = (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > qw0);
@@ -333,6 +349,28 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
   // Lane (query m, quarter g) holds d = 16dt + 4g .. +3 of its row; rows past
   // N are dropped by the stores.
+  if constexpr (SPLITKV) {
+    // A row that saw no key in this range has l = 0: O = 0 and LSE = -inf,
+    // which the merge weights by zero.  Partial rows r0 .. r0 + cnt - 1 of
+    // the head.
+    const int r0 = qt * BQ, cnt = min(BQ, N - r0);
+    const size_t prow = (size_t)split * a.part_rows + (size_t)bh * N + r0 - a.part_row_base;
+    const brsrc_t ro = make_rsrc(a.part_o + prow * D, (uint32_t)cnt * D * 4);
+    const brsrc_t rl = make_rsrc(a.part_lse + prow, (uint32_t)cnt * 4);
+    const int row = qrow - r0;
+    const float lt = sum4(l_run);
+    const float ll = BF16 ? sum4(l32_run) : lt;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      u32x4 w;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w[t] = __float_as_uint(oacc[dt][t] * inv);
+      bstore16(w, ro, ((uint32_t)row * D + (uint32_t)(16 * dt + 4 * g)) * 4u, 0);
+    }
+    if (g == 0) bstore4(ll > 0.f ? (m_run + fast_log2(ll)) * kLn2 : -INFINITY, rl, (uint32_t)row * 4u, 0);
+    return;
+  }
   const brsrc_t ro = make_rsrc((const char*)a.o + base * (OUT_F32 ? 4 : 2), (uint32_t)N * D * (OUT_F32 ? 4 : 2));
   const brsrc_t rl = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
   const float lt = sum4(l_run);
@@ -355,7 +393,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   if (g == 0) bstore4((m_run + fast_log2(ll)) * kLn2, rl, (uint32_t)qrow * 4u, 0);
 }
 
-template <bool BF16, bool CAUSAL, bool OUT_F32>
+template <bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
 hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a{};
   a.q = (const uint16_t*)p.q;
@@ -367,23 +405,48 @@ hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
   a.BH = p.BH;
   a.n_qtiles = (p.N + kBQ256 - 1) / kBQ256;
   a.c = p.scale * kLog2e;
-  a.splits = 1;
+  a.splits = SPLITKV ? p.splits : 1;
+  a.part_row_base = SPLITKV ? p.part_row_base : 0;
+  a.part_rows = SPLITKV ? (p.part_rows > 0 ? p.part_rows : p.BH * p.N) : 0;
+  a.part_o = SPLITKV ? p.part : nullptr;
+  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * a.part_rows * 256 : nullptr;
   a.item_base = CAUSAL ? 0 : p.item_base;
   const int n_items = p.item_count > 0 ? p.item_count : a.BH * a.n_qtiles - a.item_base;
-  hipLaunchKernelGGL((fwd256_kernel<BF16, CAUSAL, OUT_F32>), dim3((unsigned)n_items), dim3(kT256), 0, stream, a);
-  return hipGetLastError();
+  hipLaunchKernelGGL((fwd256_kernel<BF16, CAUSAL, SPLITKV ? false : OUT_F32, SPLITKV>),
+                     dim3((unsigned)(n_items * a.splits)), dim3(kT256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if constexpr (!SPLITKV) {
+    return e;
+  } else {
+    if (e != hipSuccess) return e;
+    // merge the partial rows into rows part_row_base .. of O and LSE
+    const int rows = a.part_rows;
+    constexpr int RPB = 256 / (256 / 4);
+    void* o_rows = (char*)p.o + (size_t)a.part_row_base * 256 * (OUT_F32 ? 4 : 2);
+    hipLaunchKernelGGL((fwd_merge_kernel<256, BF16, OUT_F32>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(256), 0, stream, a.part_o, a.part_lse, o_rows, p.lse + a.part_row_base, rows,
+                       p.splits);
+    return hipGetLastError();
+  }
 }
 
-inline hipError_t launch_fwd256(const FwdProblem& p, hipStream_t s) {
+template <bool SPLITKV>
+hipError_t launch_fwd256(const FwdProblem& p, hipStream_t s) {
   const bool bf16 = p.dtype == kBF16 || p.dtype == kBF16OutF32;
   const bool f32 = p.dtype == kF16OutF32 || p.dtype == kBF16OutF32;
   if (p.dtype < kF16 || p.dtype > kBF16OutF32) return hipErrorInvalidValue;
   if (bf16) {
-    if (f32) return p.causal ? launch_fwd256_t<true, true, true>(p, s) : launch_fwd256_t<true, false, true>(p, s);
-    return p.causal ? launch_fwd256_t<true, true, false>(p, s) : launch_fwd256_t<true, false, false>(p, s);
+    if (f32)
+      return p.causal ? launch_fwd256_t<true, true, true, SPLITKV>(p, s)
+                      : launch_fwd256_t<true, false, true, SPLITKV>(p, s);
+    return p.causal ? launch_fwd256_t<true, true, false, SPLITKV>(p, s)
+                    : launch_fwd256_t<true, false, false, SPLITKV>(p, s);
   }
-  if (f32) return p.causal ? launch_fwd256_t<false, true, true>(p, s) : launch_fwd256_t<false, false, true>(p, s);
-  return p.causal ? launch_fwd256_t<false, true, false>(p, s) : launch_fwd256_t<false, false, false>(p, s);
+  if (f32)
+    return p.causal ? launch_fwd256_t<false, true, true, SPLITKV>(p, s)
+                    : launch_fwd256_t<false, false, true, SPLITKV>(p, s);
+  return p.causal ? launch_fwd256_t<false, true, false, SPLITKV>(p, s)
+                  : launch_fwd256_t<false, false, false, SPLITKV>(p, s);
 }
 
 }  // namespace fa

@@ -3,7 +3,7 @@
 // 1: additive bias, 2: split-KV).  The build compiles this file once per
 // slice, so the nine slices compile in parallel.
 #include "fa_fwd.hpp"
-#if FA_INST_D == 256 && FA_INST_KIND == 0 && FA_FWD256_WIDE
+#if FA_INST_D == 256 && FA_INST_KIND != 1
 #include "fa_fwd256.hpp"
 #endif
 
@@ -17,8 +17,9 @@
 namespace fa {
 
 hipError_t FA_INST_NAME(FA_INST_D, FA_INST_KIND)(const FwdProblem& p, hipStream_t s) {
-#if FA_INST_D == 256 && FA_INST_KIND == 0 && FA_FWD256_WIDE
-  return launch_fwd256(p, s);  // plain d=256: the two-waves-per-SIMD kernel
+#if FA_INST_D == 256 && FA_INST_KIND != 1
+  // plain and split-KV d=256: the two-waves-per-SIMD kernel
+  return launch_fwd256<FA_INST_KIND == 2>(p, s);
 #else
   return launch_fwd_d<FA_INST_D, FA_INST_KIND == 2, FA_INST_KIND == 1>(p, s);
 #endif

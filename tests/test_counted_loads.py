@@ -3,7 +3,7 @@ loads of their key or query loop as inline assembly and count the waits
 themselves.  The compiler does not see those loads, so any vmcnt wait it
 inserted inside the loop would miscount them (and a vmcnt(0) would drain the
 whole pipeline).  Compile the d = 64 forward and backward slices and the
-d = 256 forward slice to assembly and check that no compiler-inserted vmcnt
+d = 256 plain and split-KV forward slices to assembly and check that no compiler-inserted vmcnt
 wait appears at or after the first loop header of any such kernel.  Waits
 written in the sources sit between the assembler's inline-asm markers and are
 skipped."""
@@ -61,7 +61,8 @@ def test_detector_on_a_sample():
 @pytest.mark.parametrize("src,extra,kernel", [
     ("fa_fwd_inst.hip", ["-DFA_INST_D=64", "-DFA_INST_KIND=1"], BIAS_KERNEL),
     ("fa_bwd_inst.hip", ["-DFA_INST_D=64"], BIAS_KERNEL),
-    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=0"], FWD256_KERNEL)])
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=0"], FWD256_KERNEL),
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=2"], FWD256_KERNEL)])
 def test_counted_loops_have_no_compiler_vmcnt_waits(tmp_path, src, extra, kernel):
     try:
         hipcc = build.hipcc()
@@ -75,6 +76,6 @@ def test_counted_loops_have_no_compiler_vmcnt_waits(tmp_path, src, extra, kernel
     assert res.returncode == 0, res.stderr[-2000:]
     with open(out) as f:
         found = compiler_waits_in_loop(f.read(), kernel)
-    assert len(found) >= 8, sorted(found)
+    assert len(found) >= 4, sorted(found)
     bad = {k: v for k, v in found.items() if v}
     assert not bad, bad

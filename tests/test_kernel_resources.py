@@ -62,9 +62,11 @@ def test_bias_forwards_do_not_spill(report, name):
     assert r["scratch_bytes_per_lane"] == 0, (name, r)
 
 
-# The d = 256 forward counts its K/V loads the same way.
-FWD256 = [f"void fa::fwd256_kernel<{bf}, {c}, {o}>(fa::FwdArgs)"
+# The d = 256 forward (plain and split-KV) counts its K/V loads the same way.
+FWD256 = [f"void fa::fwd256_kernel<{bf}, {c}, {o}, false>(fa::FwdArgs)"
           for bf in ("false", "true") for c in ("false", "true") for o in ("false", "true")]
+FWD256 += [f"void fa::fwd256_kernel<{bf}, {c}, false, true>(fa::FwdArgs)"
+           for bf in ("false", "true") for c in ("false", "true")]
 
 
 @pytest.mark.parametrize("name", FWD256)
