@@ -88,8 +88,12 @@ namespace fa {
 // next tile's loads before the first LDS read of each iteration was fully
 // exposed: counted loads measured -16% (B2 H8 N4096 fp16), -14% (bf16) and
 // -12% (bf16 causal, fp32 O), bit-identical.
-// Unbiased d=256 forwards (plain and split-KV) run fwd256_kernel
-// (fa_fwd256.hpp); fwd_kernel<256> serves the biased one.
+// Unbiased d=256 forwards (plain and split-KV) run fwd_q16_kernel
+// (fa_fwd_q16.hpp); fwd_kernel<256> serves the biased one.  FA_FWD128_Q16
+// routes the unbiased d=128 forwards there too.
+#ifndef FA_FWD128_Q16
+#define FA_FWD128_Q16 1
+#endif
 #ifndef FA_FWD256_COUNTED
 #define FA_FWD256_COUNTED 1
 #endif

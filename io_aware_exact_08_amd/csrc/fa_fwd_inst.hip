@@ -3,8 +3,11 @@
 // 1: additive bias, 2: split-KV).  The build compiles this file once per
 // slice, so the nine slices compile in parallel.
 #include "fa_fwd.hpp"
-#if FA_INST_D == 256 && FA_INST_KIND != 1
-#include "fa_fwd256.hpp"
+#if FA_INST_KIND != 1 && (FA_INST_D == 256 || (FA_INST_D == 128 && FA_FWD128_Q16))
+#define FA_INST_Q16 1
+#include "fa_fwd_q16.hpp"
+#else
+#define FA_INST_Q16 0
 #endif
 
 #if !defined(FA_INST_D) || !defined(FA_INST_KIND)
@@ -17,9 +20,25 @@
 namespace fa {
 
 hipError_t FA_INST_NAME(FA_INST_D, FA_INST_KIND)(const FwdProblem& p, hipStream_t s) {
-#if FA_INST_D == 256 && FA_INST_KIND != 1
-  // plain and split-KV d=256: the two-waves-per-SIMD kernel
-  return launch_fwd256<FA_INST_KIND == 2>(p, s);
+#if FA_INST_Q16 && FA_INST_D == 256
+  // unbiased d=256: the 16-query-wave kernel
+  return launch_fwd_q16<256, FA_INST_KIND == 2>(p, s);
+#elif FA_INST_Q16
+  // unbiased d=128: bf16 on the 16-query-wave kernel; fp16 keeps fwd_kernel,
+  // whose lazy softmax (no row max on the common path) needs more registers
+  // than the 16-query kernel has at four waves per SIMD
+  constexpr bool SPLIT = FA_INST_KIND == 2;
+  switch (p.dtype) {
+    case kF16: return launch_fwd_c<128, false, false, SPLIT, false>(p, s);
+    case kF16OutF32: return launch_fwd_c<128, false, true, SPLIT, false>(p, s);
+    case kBF16:
+      return p.causal ? launch_fwd_q16_t<128, true, true, false, SPLIT>(p, s)
+                      : launch_fwd_q16_t<128, true, false, false, SPLIT>(p, s);
+    case kBF16OutF32:
+      return p.causal ? launch_fwd_q16_t<128, true, true, true, SPLIT>(p, s)
+                      : launch_fwd_q16_t<128, true, false, true, SPLIT>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 #else
   return launch_fwd_d<FA_INST_D, FA_INST_KIND == 2, FA_INST_KIND == 1>(p, s);
 #endif

@@ -1,32 +1,36 @@
-// Fused exact-attention forward for head dimension 256 on 16x16x32 MFMAs.
+// Fused exact-attention forward for head dimensions 128 and 256 on 16x16x32
+// MFMAs with 16-query waves.
 //
 // The method is fwd_kernel's (page 2 of the subject, "Kernel Fusion" and
 // "Tiling": scores, online softmax and P V per tile, one normalisation at the
 // end, O and the row LSE written once).  What changes is the mapping, chosen
-// so that two waves fit each SIMD at d = 256:
-//  * A workgroup is 8 waves (two per SIMD) of 16 query rows each, 128 rows in
-//    all.  A wave's O^T (256 d x 16 queries) is 16 accumulator tiles of four
+// so that the registers of a wave shrink (two waves fit each SIMD at d = 256):
+//  * A workgroup is 8 waves of 16 query rows each, 128 rows in all.  At
+//    d = 256 a wave's O^T (256 d x 16 queries) is 16 accumulator tiles of four
 //    registers, 64 in all, and its Q^T operand 32 registers; with 32 queries
 //    per wave (fwd_kernel) O alone takes 128 and the accumulators had to be
-//    parked in the accumulation registers around every product.
+//    parked in the accumulation registers around every product.  At d = 128
+//    both halve.
 //  * S^T = K Q^T per 16-key block with v_mfma_f32_16x16x32: lane l holds
 //    query l%16 and keys 4(l/16) .. 4(l/16)+3 of the block.  A row's 32 keys
 //    of a tile sit in lanes l%16 + 16g, g = 0..3, so its max and sum combine
 //    over those four lanes (ds_swizzle for the xor-16 pair, permlane32_swap
 //    for the halves).  Every O register of a lane belongs to its query, so a
-//    rescale multiplies the lane's 64 accumulators by one factor, and the row
+//    rescale multiplies the lane's accumulators by one factor, and the row
 //    max is cheap enough to take on every tile (one exponential/P V path for
 //    both input types).
 //  * The lane's eight probabilities of a tile (keys 4g+j and 16+4g+j, j < 4)
 //    are exactly the eight k-slots it supplies to O^T += V^T P^T; the V^T
 //    operand is read with ds_read_b64_tr_b16 from the same two groups of four
 //    keys, so P goes from the score registers to the next product directly.
-//  * K and V tiles of 32 keys stream through four LDS stages (128 KB) by
-//    direct buffer->LDS loads that the kernel counts itself (the compiler would
-//    otherwise wait for all of them before every LDS read).  K rows are
-//    swizzled so that the 16 lanes reading one chunk of 16 consecutive rows
-//    hit 16 bank slots; V rows so that the transposing read's 32 lanes of a
-//    cycle (8 rows x 2 chunks) do.
+//  * K and V tiles of 32 keys stream through four LDS stages (128 KB at
+//    d = 256, 64 KB at d = 128) by direct buffer->LDS loads that the kernel
+//    counts itself (the compiler would otherwise wait for all of them before
+//    every LDS read).  K rows are swizzled so that the 16 lanes reading one
+//    chunk of 16 consecutive rows hit 16 bank slots; V rows so that the
+//    transposing read's 32 lanes of a cycle (8 rows x 2 chunks) do.  Both
+//    XORs stay inside a 256-byte bank window, which a row fills at d = 128
+//    and half fills at d = 256.
 #pragma once
 
 #include "fa_fwd.hpp"
@@ -60,35 +64,45 @@ __device__ __forceinline__ void bstore8(u32x2 v, brsrc_t r, uint32_t voff, uint3
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
 }
 
-constexpr int kW256 = 8;              // waves per workgroup (two per SIMD)
-constexpr int kT256 = kW256 * 64;     // threads
-constexpr int kBQ256 = kW256 * 16;    // query rows per workgroup
-constexpr int kBK256 = 32;            // keys per tile
-constexpr int kSt256 = 4;             // LDS stages
-static_assert(kBQ256 == kWaves * FwdCfg<256>::QB * 32, "query tile seen by the split plan");
-
-#ifndef FA_FWD256W_LA
-#define FA_FWD256W_LA 4
+constexpr int kWQ16 = 8;              // waves per workgroup
+constexpr int kTQ16 = kWQ16 * 64;     // threads
+constexpr int kBQQ16 = kWQ16 * 16;    // query rows per workgroup
+constexpr int kBKQ16 = 32;            // keys per tile
+constexpr int kStQ16 = 4;             // LDS stages
+static_assert(kBQQ16 == kWaves * FwdCfg<256>::QB * 32 && kBQQ16 == kWaves * FwdCfg<128>::QB * 32,
+              "query tile seen by the split plan");
+#ifndef FA_FWDQ16_LA
+#define FA_FWDQ16_LA 4
 #endif
+#ifndef FA_FWDQ16_128_WAVES
+#define FA_FWDQ16_128_WAVES 4
+#endif
+// waves per SIMD the launch bounds ask the register allocation to allow: one
+// workgroup (two waves per SIMD) per CU at d = 256, whose stages take 128 KB
+// of LDS; two at d = 128 (64 KB each)
+template <int D>
+constexpr int q16_min_waves() { return D == 256 ? 2 : FA_FWDQ16_128_WAVES; }
 
 // SPLITKV: the key tiles of each query tile are cut into a.splits ranges and
 // each workgroup writes its range's O (fp32, normalised by its own sum) and
 // LSE as partial rows, which fwd_merge_kernel combines (OUT_F32 unused).
-template <bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
-__global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
-  constexpr int D = 256;
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
+__global__ __launch_bounds__(kTQ16, q16_min_waves<D>()) void fwd_q16_kernel(FwdArgs a) {
+  static_assert(D == 128 || D == 256, "the swizzles assume rows of one or two bank windows");
   constexpr int ROWB = D * 2;                     // bytes per K/V row
-  constexpr int BK = kBK256, BQ = kBQ256;
+  constexpr int BK = kBKQ16, BQ = kBQQ16;
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int LOADS = BK * CPR / kT256;         // direct loads per thread per tensor
-  static_assert(LOADS * kT256 == BK * CPR, "tile split");
+  constexpr int DC = D / 32;                      // Q^T register groups (contraction of S^T)
+  constexpr int DT = D / 16;                      // O^T accumulator tiles
+  constexpr int LOADS = BK * CPR / kTQ16;         // direct loads per thread per tensor
+  static_assert(LOADS * kTQ16 == BK * CPR, "tile split");
   constexpr int kTileLoads = 2 * LOADS;           // per thread per tile (K and V)
-  constexpr int kAhead = kSt256 - 1;              // prefetch distance in tiles
+  constexpr int kAhead = kStQ16 - 1;              // prefetch distance in tiles
   constexpr int STAGEB = BK * ROWB;               // bytes per stage and tensor
-  constexpr int LA = FA_FWD256W_LA;
+  constexpr int LA = FA_FWDQ16_LA;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kSt256][BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kSt256][BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kStQ16][BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kStQ16][BK * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,13 +138,13 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   // Q^T operand (B of S^T = K Q^T): register group dc holds d = 32dc + 8g ..
   // +7 of this lane's query row (rows past N read as 0).  Settled before the
   // loop, whose loads the compiler does not see.
-  u32x4 qf[8];
+  u32x4 qf[DC];
   {
     const brsrc_t rq = make_rsrc(a.q + base, head_bytes);
 #pragma unroll
-    for (int dc = 0; dc < 8; ++dc) qf[dc] = bload16(rq, ((uint32_t)qrow * D + 32 * dc + 8 * g) * 2u, 0);
+    for (int dc = 0; dc < DC; ++dc) qf[dc] = bload16(rq, ((uint32_t)qrow * D + 32 * dc + 8 * g) * 2u, 0);
 #pragma unroll
-    for (int dc = 0; dc < 8; ++dc) settle(qf[dc]);
+    for (int dc = 0; dc < DC; ++dc) settle(qf[dc]);
   }
 
   // K operand (A): key m of a 16-key block, chunk 4dc + g, stored at chunk
@@ -154,12 +168,12 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   }
   auto v_off = [&](int dt) { return vr[dt & 7] + (dt >> 3) * 256; };
 
-  // Direct-load slots: thread slot p = i * kT256 + tid holds tile row p / CPR
+  // Direct-load slots: thread slot p = i * kTQ16 + tid holds tile row p / CPR
   // at chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
   uint32_t k_gl[LOADS], v_gl[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int p = i * kT256 + tid;
+    const int p = i * kTQ16 + tid;
     const int row = p / CPR, pos = p % CPR;
     k_gl[i] = (uint32_t)(row * ROWB + ((pos ^ (row & 15)) * 16));
     v_gl[i] = (uint32_t)(row * ROWB + ((pos ^ ((row & 7) << 1)) * 16));
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
         (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(j0 + j) * (uint32_t)STAGEB));
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const uint32_t slot = (uint32_t)(st * STAGEB + (i * kT256 + wave * 64) * 16);
+      const uint32_t slot = (uint32_t)(st * STAGEB + (i * kTQ16 + wave * 64) * 16);
       bload16_lds_asm(wk, lds_k + slot, k_gl[i], soff);
       bload16_lds_asm(wv, lds_v + slot, v_gl[i], soff);
     }
@@ -195,9 +209,9 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   // share of the sum of the rounded probabilities; l32_run: its fp32 sum (bf16
   // LSE).
   float m_run = -INFINITY, l_run = 0.f, l32_run = 0.f;
-  f32x4 oacc[16];
+  f32x4 oacc[DT];
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // S^T of one K tile: s[kb][r] is key 16kb + 4g + r of the tile.
   struct S2 {
@@ -210,10 +224,10 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int dc = 0; dc < 8; ++dc) {
+      for (int dc = 0; dc < DC; ++dc) {
         const u32x4 ka = *(const u32x4*)(Kb + kb * 16 * ROWB + k_off(dc));
         s.v[kb] = mfma16<BF16>(ka, qf[dc], s.v[kb]);
-        pin_step<1, 1, LA>(kb * 8 + dc);
+        pin_step<1, 1, LA>(kb * DC + dc);
       }
     pin_tail<1, LA>();
     return s;
@@ -222,7 +236,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   // 4g + i for i < 4, 16 + 4g + i - 4 after).
   auto pv = [&](const char* Vb, const u32x4& pf) {
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
       const u32x2 lo = lds_read_tr16(Vb + v_off(dt));
       const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + 16 * ROWB);
       const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   auto rescale_pv = [&](const char* Vb, const u32x4& pf, float alpha, bool grow) {
     if (__ballot(grow) != 0ull) {
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
     pv(Vb, pf);
   };
@@ -301,8 +315,8 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   S2 s_cur;
   auto iteration = [&](int j, auto stage_tag) {
     constexpr int st = decltype(stage_tag)::value;
-    constexpr int st1 = (st + 1) % kSt256;
-    if (j + kAhead < n_kt) issue_tile(j + kAhead, (st + kAhead) % kSt256);
+    constexpr int st1 = (st + 1) % kStQ16;
+    if (j + kAhead < n_kt) issue_tile(j + kAhead, (st + kAhead) % kStQ16);
     const int k0 = (j0 + j) * BK;
     const bool active = !CAUSAL || (k0 <= qw0 + 15);
     if (active) {
@@ -322,7 +336,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
       s_cur = s_next;
     }
     if (j + kAhead < n_kt) {
-      wait_vmem_keep<(kSt256 - 3) * kTileLoads>();
+      wait_vmem_keep<(kStQ16 - 3) * kTileLoads>();
     } else {
       wait_vmem();
     }
@@ -333,13 +347,13 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   for (int s0 = 0; s0 < kAhead; ++s0)
     if (s0 < n_kt) issue_tile(s0, s0);
   if (kAhead < n_kt) {
-    wait_vmem_keep<(kSt256 - 3) * kTileLoads>();  // tiles 0 and 1 have landed
+    wait_vmem_keep<(kStQ16 - 3) * kTileLoads>();  // tiles 0 and 1 have landed
   } else {
     wait_vmem();
   }
   barrier_no_fence();
   s_cur = scores((const char*)sK[0]);
-  for (int j = 0; j < n_kt; j += kSt256) {
+  for (int j = 0; j < n_kt; j += kStQ16) {
     iteration(j, std::integral_constant<int, 0>{});
     if (j + 1 < n_kt) iteration(j + 1, std::integral_constant<int, 1>{});
     if (j + 2 < n_kt) iteration(j + 2, std::integral_constant<int, 2>{});
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
     const float ll = BF16 ? sum4(l32_run) : lt;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
       u32x4 w;
 #pragma unroll
       for (int t = 0; t < 4; ++t) w[t] = __float_as_uint(oacc[dt][t] * inv);
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   const float ll = BF16 ? sum4(l32_run) : lt;
   const float inv = 1.0f / lt;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
     const uint32_t col = (uint32_t)(16 * dt + 4 * g);
     if constexpr (OUT_F32) {
       u32x4 w;
@@ -393,8 +407,8 @@ __global__ __launch_bounds__(kT256, 1) void fwd256_kernel(FwdArgs a) {
   if (g == 0) bstore4((m_run + fast_log2(ll)) * kLn2, rl, (uint32_t)qrow * 4u, 0);
 }
 
-template <bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
-hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
+template <int D, bool BF16, bool CAUSAL, bool OUT_F32, bool SPLITKV>
+hipError_t launch_fwd_q16_t(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a{};
   a.q = (const uint16_t*)p.q;
   a.k = (const uint16_t*)p.k;
@@ -403,17 +417,17 @@ hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
   a.lse = p.lse;
   a.N = p.N;
   a.BH = p.BH;
-  a.n_qtiles = (p.N + kBQ256 - 1) / kBQ256;
+  a.n_qtiles = (p.N + kBQQ16 - 1) / kBQQ16;
   a.c = p.scale * kLog2e;
   a.splits = SPLITKV ? p.splits : 1;
   a.part_row_base = SPLITKV ? p.part_row_base : 0;
   a.part_rows = SPLITKV ? (p.part_rows > 0 ? p.part_rows : p.BH * p.N) : 0;
   a.part_o = SPLITKV ? p.part : nullptr;
-  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * a.part_rows * 256 : nullptr;
+  a.part_lse = SPLITKV ? p.part + (size_t)p.splits * a.part_rows * D : nullptr;
   a.item_base = CAUSAL ? 0 : p.item_base;
   const int n_items = p.item_count > 0 ? p.item_count : a.BH * a.n_qtiles - a.item_base;
-  hipLaunchKernelGGL((fwd256_kernel<BF16, CAUSAL, SPLITKV ? false : OUT_F32, SPLITKV>),
-                     dim3((unsigned)(n_items * a.splits)), dim3(kT256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_q16_kernel<D, BF16, CAUSAL, SPLITKV ? false : OUT_F32, SPLITKV>),
+                     dim3((unsigned)(n_items * a.splits)), dim3(kTQ16), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if constexpr (!SPLITKV) {
     return e;
@@ -421,32 +435,32 @@ hipError_t launch_fwd256_t(const FwdProblem& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     // merge the partial rows into rows part_row_base .. of O and LSE
     const int rows = a.part_rows;
-    constexpr int RPB = 256 / (256 / 4);
-    void* o_rows = (char*)p.o + (size_t)a.part_row_base * 256 * (OUT_F32 ? 4 : 2);
-    hipLaunchKernelGGL((fwd_merge_kernel<256, BF16, OUT_F32>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+    constexpr int RPB = 256 / (D / 4);
+    void* o_rows = (char*)p.o + (size_t)a.part_row_base * D * (OUT_F32 ? 4 : 2);
+    hipLaunchKernelGGL((fwd_merge_kernel<D, BF16, OUT_F32>), dim3((unsigned)((rows + RPB - 1) / RPB)),
                        dim3(256), 0, stream, a.part_o, a.part_lse, o_rows, p.lse + a.part_row_base, rows,
                        p.splits);
     return hipGetLastError();
   }
 }
 
-template <bool SPLITKV>
-hipError_t launch_fwd256(const FwdProblem& p, hipStream_t s) {
+template <int D, bool SPLITKV>
+hipError_t launch_fwd_q16(const FwdProblem& p, hipStream_t s) {
   const bool bf16 = p.dtype == kBF16 || p.dtype == kBF16OutF32;
   const bool f32 = p.dtype == kF16OutF32 || p.dtype == kBF16OutF32;
   if (p.dtype < kF16 || p.dtype > kBF16OutF32) return hipErrorInvalidValue;
   if (bf16) {
     if (f32)
-      return p.causal ? launch_fwd256_t<true, true, true, SPLITKV>(p, s)
-                      : launch_fwd256_t<true, false, true, SPLITKV>(p, s);
-    return p.causal ? launch_fwd256_t<true, true, false, SPLITKV>(p, s)
-                    : launch_fwd256_t<true, false, false, SPLITKV>(p, s);
+      return p.causal ? launch_fwd_q16_t<D, true, true, true, SPLITKV>(p, s)
+                      : launch_fwd_q16_t<D, true, false, true, SPLITKV>(p, s);
+    return p.causal ? launch_fwd_q16_t<D, true, true, false, SPLITKV>(p, s)
+                    : launch_fwd_q16_t<D, true, false, false, SPLITKV>(p, s);
   }
   if (f32)
-    return p.causal ? launch_fwd256_t<false, true, true, SPLITKV>(p, s)
-                    : launch_fwd256_t<false, false, true, SPLITKV>(p, s);
-  return p.causal ? launch_fwd256_t<false, true, false, SPLITKV>(p, s)
-                  : launch_fwd256_t<false, false, false, SPLITKV>(p, s);
+    return p.causal ? launch_fwd_q16_t<D, false, true, true, SPLITKV>(p, s)
+                    : launch_fwd_q16_t<D, false, false, true, SPLITKV>(p, s);
+  return p.causal ? launch_fwd_q16_t<D, false, true, false, SPLITKV>(p, s)
+                  : launch_fwd_q16_t<D, false, false, false, SPLITKV>(p, s);
 }
 
 }  // namespace fa

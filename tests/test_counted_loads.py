@@ -1,12 +1,12 @@
-"""The bias kernels (d = 64, 128) and the d = 256 forward issue the direct
-loads of their key or query loop as inline assembly and count the waits
-themselves.  The compiler does not see those loads, so any vmcnt wait it
-inserted inside the loop would miscount them (and a vmcnt(0) would drain the
-whole pipeline).  Compile the d = 64 forward and backward slices and the
-d = 256 plain and split-KV forward slices to assembly and check that no compiler-inserted vmcnt
-wait appears at or after the first loop header of any such kernel.  Waits
-written in the sources sit between the assembler's inline-asm markers and are
-skipped."""
+"""The bias kernels (d = 64, 128) and the 16-query-wave forward (d = 256 and
+bf16 d = 128) issue the direct loads of their key or query loop as inline
+assembly and count the waits themselves.  The compiler does not see those
+loads, so any vmcnt wait it inserted inside the loop would miscount them (and
+a vmcnt(0) would drain the whole pipeline).  Compile the d = 64 forward and
+backward slices and the d = 256 (plain, split-KV) and d = 128 forward slices
+to assembly and check that no compiler-inserted vmcnt wait appears at or after
+the first loop header of any such kernel.  Waits written in the sources sit
+between the assembler's inline-asm markers and are skipped."""
 import os
 import re
 import subprocess
@@ -16,7 +16,7 @@ import pytest
 from io_aware_exact_08_amd import build
 
 BIAS_KERNEL = re.compile(r"^(_ZN2fa\d+(?:fwd_kernel|bwd_dkdv_kernel|bwd_dq_kernel)I\S*ELb1EEEvNS_7[FB]wdArgsE):")
-FWD256_KERNEL = re.compile(r"^(_ZN2fa13fwd256_kernelI\S*EEvNS_7FwdArgsE):")
+Q16_KERNEL = re.compile(r"^(_ZN2fa14fwd_q16_kernelI\S*EEvNS_7FwdArgsE):")
 
 
 def compiler_waits_in_loop(asm_text, kernel=BIAS_KERNEL):
@@ -61,8 +61,9 @@ def test_detector_on_a_sample():
 @pytest.mark.parametrize("src,extra,kernel", [
     ("fa_fwd_inst.hip", ["-DFA_INST_D=64", "-DFA_INST_KIND=1"], BIAS_KERNEL),
     ("fa_bwd_inst.hip", ["-DFA_INST_D=64"], BIAS_KERNEL),
-    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=0"], FWD256_KERNEL),
-    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=2"], FWD256_KERNEL)])
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=0"], Q16_KERNEL),
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=256", "-DFA_INST_KIND=2"], Q16_KERNEL),
+    ("fa_fwd_inst.hip", ["-DFA_INST_D=128", "-DFA_INST_KIND=0"], Q16_KERNEL)])
 def test_counted_loops_have_no_compiler_vmcnt_waits(tmp_path, src, extra, kernel):
     try:
         hipcc = build.hipcc()
