@@ -37,6 +37,20 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
+// C[16x16] += A[16x32] * B[32x16], fp32 accumulate.  Lane l supplies row
+// (l%16) of A and column (l%16) of B, eight k-values each (k = 8(l/16) + i);
+// lane l receives column l%16, rows 4(l/16) .. 4(l/16)+3.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
 // Raw buffer access.  A resource covers [base, base + bytes); loads outside it
 // return 0 and stores outside it are dropped by the hardware, which handles
 // ragged tails without branches.
@@ -52,6 +66,9 @@ __device__ __forceinline__ u32x4 bload16(brsrc_t r, uint32_t voff, uint32_t soff
 __device__ __forceinline__ void bstore16(u32x4 v, brsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v),
                                          r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore8(u32x2 v, brsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ void bstore4(float v, brsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
@@ -181,6 +198,14 @@ __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The value of lane l ^ 16 (ds_swizzle in bit mode: and 0x1f, or 0, xor 0x10,
+// within each 32-lane half).
+__device__ __forceinline__ float swap16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+}
+// Max and sum over lanes l, l^16, l^32, l^48 (identical in all four).
+__device__ __forceinline__ float max4(float x) { return max_halves(fmaxf(x, swap16(x))); }
+__device__ __forceinline__ float sum4(float x) { return sum_halves(x + swap16(x)); }
 
 // Row permutation applied when loading the A operand of a 32x32 MFMA so that
 // the output's register r of lane half h maps to row 16*(r/8) + 8*h + r%8:
