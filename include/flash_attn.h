@@ -27,8 +27,8 @@
  *    anything is enqueued; on a non-zero status nothing was launched.
  *  - Sizes: B, H, N >= 1, any N (tail tiles are masked); head dimension d in
  *    {64, 128, 256} (page 2, "工程落地的关键考量", hardware requirements,
- *    names 64, 128 and 256 as the preferred head sizes), except
- *    flash_attn_bwd_bias: {64, 128}; B*H*N*d < 2^31 elements per tensor, and
+ *    names 64, 128 and 256 as the preferred head sizes); B*H*N*d < 2^31
+ *    elements per tensor, and
  *    (N + 256) * d * s < 2^32 bytes for every per-head output with elements
  *    of s bytes (s = 4 for a float32 O and for the split-KV partials, 2 for
  *    16-bit O, dQ, dK, dV): the kernels address a head through a 32-bit byte
@@ -55,8 +55,7 @@ typedef enum {
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, a tensor of 2^31 elements or more,
                            a per-head output range of 2^32 bytes or more, or
                            causal not 0/1                                     */
-  FA_ERR_HEADDIM = 3,   /* d not in {64,128,256} ({64,128} for the backward
-                           with an attention bias)                          */
+  FA_ERR_HEADDIM = 3,   /* d not in {64,128,256}                            */
   FA_ERR_DTYPE = 4,     /* unknown fa_dtype                                 */
   FA_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned                 */
   FA_ERR_LAUNCH = 6,    /* the HIP runtime rejected a kernel launch         */
@@ -130,9 +129,7 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * the LSE flash_attn_fwd_bias wrote (the bias is a constant: its own
  * gradient, dS, is not formed).  Rows whose every key is hidden contribute
  * nothing.  Arguments as flash_attn_bwd, plus bias and its strides exactly as
- * passed to flash_attn_fwd_bias (same checks); d must be 64 or 128
- * (FA_ERR_HEADDIM for 256: two dK/dV tile stages with the bias block would
- * exceed the compute unit's 160 KB of LDS).
+ * passed to flash_attn_fwd_bias (same checks).
  */
 int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void* bias,
                         long long bias_stride_b, long long bias_stride_h, const void* o,

@@ -9,8 +9,7 @@ module only marshals torch tensors (device memory and streams) into its C ABI:
     flash_attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
     flash_attn_bwd_bias(q, k, v, bias, o, lse, dout, causal=False, scale=None) -> (dq, dk, dv)
 
-Layout [B, H, N, d], d in {64, 128, 256} ({64, 128} for the backward with a bias),
-fp16 or bf16 inputs.
+Layout [B, H, N, d], d in {64, 128, 256}, fp16 or bf16 inputs.
 """
 from __future__ import annotations
 

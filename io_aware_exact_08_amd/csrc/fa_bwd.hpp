@@ -217,15 +217,10 @@ template <int D>
 __host__ __device__ constexpr int dkdv_stage_bytes() {
   return 2 * dkdv_bq<D>() * D * 2 + 2 * dkdv_bq<D>() * 4;  // Q, dO tiles + LSE2, D rows
 }
-// With an attention bias a stage also holds the bias block of the tile's 64
-// query rows x the workgroup's 128 keys (row-major, 256 bytes per row).
-constexpr int kDkvBiasRowBytes = kDkvKeys * 2;
-constexpr int kDkvBiasBytes = kDkvBQ * kDkvBiasRowBytes;
 
 template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BQ = dkdv_bq<D>();
-  static_assert(!BIAS || BQ == kDkvBQ, "the bias block is sized for 64-row tiles");
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int QT = BQ / 32;  // 32-row query sub-tiles per streamed tile
@@ -236,15 +231,13 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   static_assert(LOADS * kBwdThreads == BQ * CPR, "tile split");
   // With a bias every direct load of the query loop is issued as inline
   // assembly and waited for by hand, and each wave stages its 32 key columns
-  // of the bias block two query tiles ahead in an LDS ring (see the forward:
-  // the compiler would otherwise wait for all direct loads before each LDS
-  // read).  The ring takes the place of the per-stage bias block.
-  constexpr bool kCounted = BIAS ? D <= 128
-                                 : (FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED));
-  constexpr bool kBiasLds = BIAS && kCounted;
-  constexpr int STAGE = dkdv_stage_bytes<D>() + ((BIAS && !kBiasLds) ? kDkvBiasBytes : 0);
+  // of the bias two query tiles ahead in an LDS ring behind the two stages
+  // (see the forward: the compiler would otherwise wait for all direct loads
+  // before each LDS read).
+  constexpr bool kCounted = BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED);
+  constexpr bool kBiasLds = BIAS;
+  constexpr int STAGE = dkdv_stage_bytes<D>();
   constexpr int TILE = BQ * ROWB;
-  constexpr int BIAS_OFF = dkdv_stage_bytes<D>();  // bias block within a stage
   // fp16: K is pre-multiplied by c = scale*log2(e) and the S accumulators
   // start at -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the
   // exponent c*s - LSE*log2(e) itself: no multiply-add per score (a bias then
@@ -280,22 +273,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   const brsrc_t rg = make_rsrc(a.dout + base, head_bytes);
   const brsrc_t rl = make_rsrc(a.lse2 + (size_t)bh * N, (uint32_t)N * 4);
   const brsrc_t rd = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
-  const brsrc_t rb =
-      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
-                BIAS ? (uint32_t)N * N * 2 : 0u);
-  // Bias gather through the transposing read: in each 16-lane group (G), lane
-  // L supplies row R + L/4 and columns c0 + 4(L%4) .. +3 of the row-major bias
-  // block; result lane i then holds rows R..R+3 of column c0 + i.  With
-  // c0 = 32*wave + 16(G%2) and R = 32t + 16g + 8(G/2) (+4), lane l receives
-  // exactly the bias of its key (32*wave + l%32) at the query rows of score
-  // registers 8g + 0..3 (and 4..7) of sub-tile t.
-  const int bias_rd = ((lane & 15) >> 2) * kDkvBiasRowBytes + 8 * ((lane >> 5) & 1) * kDkvBiasRowBytes +
-                      (32 * wave + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   const int kw0 = kvt * kDkvKeys + wave * 32;  // first key of this wave
   const int key = kw0 + m;                     // this lane's key (column of S)
-  // The same gather from the bias ring, whose rows are this wave's 32 keys
-  // (64 bytes): four rows fill a 256-byte bank window, so the 32 lanes of a
-  // read cycle (rows R..R+3, both column halves) hit every bank slot once.
+  // Bias gather through the transposing read from the bias ring, whose rows
+  // are this wave's 32 keys (64 bytes): in each 16-lane group (G), lane L
+  // supplies row R + L/4 and columns 16(G%2) + 4(L%4) .. +3; result lane i
+  // then holds rows R..R+3 of column 16(G%2) + i.  With R = 32t + 16g +
+  // 8(G/2) (+4), lane l receives exactly the bias of its key (l%32) at the
+  // query rows of score registers 8g + 0..3 (and 4..7) of sub-tile t.  Four
+  // rows fill a 256-byte bank window, so the 32 lanes of a read cycle (rows
+  // R..R+3, both column halves) hit every bank slot once.
   constexpr int kRingRowBytes = 64;
   const int bias_rd_w = ((lane & 15) >> 2) * kRingRowBytes + 8 * ((lane >> 5) & 1) * kRingRowBytes +
                         (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
@@ -392,17 +379,6 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       if (wave == 0) bload16_lds(rl, stage + 2 * TILE, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
       if (wave == 1) bload16_lds(rd, stage + 2 * TILE + BQ * 4, (uint32_t)(lane * 16), (uint32_t)qt * (uint32_t)(BQ * 4));
     }
-    if constexpr (BIAS) {
-      // bias rows qt*BQ .. +63, columns of this workgroup's 128 keys: slot p
-      // holds row p/16, 16-byte chunk p%16 (rows past N read as 0)
-#pragma unroll
-      for (int i = 0; i < kDkvBiasBytes / 16 / kBwdThreads; ++i) {
-        const int p = i * kBwdThreads + tid;
-        const uint32_t off =
-            ((uint32_t)(qt * BQ + p / 16) * (uint32_t)N + (uint32_t)(kvt * kDkvKeys + (p % 16) * 8)) * 2u;
-        bload16_lds(rb, stage + BIAS_OFF + (i * kBwdThreads + wave * 64) * 16, off, 0u);
-      }
-    }
   };
 
   // Bias ring: wave w, slot t % 2 holds rows t*BQ .. +63 of its 32 keys
@@ -479,19 +455,16 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
       // s + bias/scale (so that c * s = scale*q.k*log2(e) + bias*log2(e));
       // with PRE the scores are already in log2 units: s + bias*log2(e)
       const float kb = PRE ? kLog2e : 1.0f / a.scale;
-      const char* sB = kBiasLds ? smem + ring_off + (wave * 2 + ((q0 / BQ) & 1)) * BQ * kRingRowBytes
-                                : stage + BIAS_OFF;
-      const int rd0 = kBiasLds ? bias_rd_w : bias_rd;
-      constexpr int pitch = kBiasLds ? kRingRowBytes : kDkvBiasRowBytes;
+      const char* sB = smem + ring_off + (wave * 2 + ((q0 / BQ) & 1)) * BQ * kRingRowBytes;
       u32x2 bv[QT][2][2];
-      if constexpr (kBiasLds) wait_vmem_keep<2 * kTileLoads + LB>();  // this tile's bias has landed
+      wait_vmem_keep<2 * kTileLoads + LB>();  // this tile's bias has landed
 #pragma unroll
       for (int t = 0; t < QT; ++t)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int half = 0; half < 2; ++half)
-            bv[t][g][half] = lds_read_tr16(sB + rd0 + (t * 32 + 16 * g + 4 * half) * pitch);
+            bv[t][g][half] = lds_read_tr16(sB + bias_rd_w + (t * 32 + 16 * g + 4 * half) * kRingRowBytes);
       after_bias();
 #pragma unroll
       for (int t = 0; t < QT; ++t)
@@ -693,9 +666,8 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   // assembly and waited for by hand, and each wave stages its bias rows two
   // key tiles ahead in an LDS ring (the forward's scheme: the compiler would
   // otherwise wait for all direct loads before each LDS read).
-  constexpr bool kCounted = BIAS ? D <= 128
-                                 : (FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED));
-  constexpr bool kBiasLds = BIAS && kCounted;
+  constexpr bool kCounted = BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED);
+  constexpr bool kBiasLds = BIAS;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -722,9 +694,6 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   const brsrc_t rv = make_rsrc(a.v + base, head_bytes);
   const int qw0 = qt * kDqRows + wave * 32;
   const int qrow = qw0 + m;
-  const brsrc_t rb =
-      make_rsrc(BIAS ? a.bias + (bh / a.H) * a.bias_sb + (bh % a.H) * a.bias_sh : a.q,
-                BIAS ? (uint32_t)N * N * 2 : 0u);
 
   // Q^T and dO^T as B operands (lane: query m; slot i: d = 16dc + 8h + i).
   u32x4 qf[DC], gf[DC];
@@ -855,20 +824,14 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
     const char* sV = stage + TILE;
     // S^T = K Q^T, dP^T - D = V dO^T - D (rows: keys with perm_k, cols:
     // queries).  Register r of key tile kt holds key kt*32 + 16(r/8) + 8h + r%8.
-    // With a bias, registers 8g..8g+7 of key tile kt need eight consecutive
-    // entries of this lane's bias row: one 16-byte load each, issued first.
+    // With a bias, registers 8g..8g+7 of key tile kt take eight consecutive
+    // entries of this lane's bias row, read from the ring before the tile.
     u32x4 bw[KT][2];
-    if constexpr (kBiasLds) {
+    if constexpr (BIAS) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int g = 0; g < 2; ++g) bw[kt][g] = bw_ring[kt][g];
-    } else if constexpr (BIAS) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-          bw[kt][g] = bload16(rb, ((uint32_t)qrow * (uint32_t)N + (uint32_t)(k0 + 32 * kt + 16 * g + 8 * h)) * 2u, 0);
     }
     f32x16 s[KT], dp[KT];
 #pragma unroll
@@ -1060,7 +1023,8 @@ template <int D, bool BF16, bool CAUSAL, bool BIAS>
 hipError_t launch_dkdv_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
-  const int lds = 2 * (dkdv_stage_bytes<D>() + (BIAS ? kDkvBiasBytes : 0));
+  // two stages, then (bias) each wave's two-slot ring of BQ rows x 64 bytes
+  const int lds = 2 * dkdv_stage_bytes<D>() + (BIAS ? (kBwdThreads / 64) * 2 * dkdv_bq<D>() * 64 : 0);
   auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
@@ -1092,26 +1056,16 @@ template <int D, bool BF16, bool X>
 struct PreL {
   static hipError_t run(const BwdProblem& p, hipStream_t s) { return launch_pre_t<D, BF16, X>(p, s); }
 };
-// (d=256 has no bias variant: two dK/dV stages with the bias block would need
-// 161 KB of LDS.)
 template <int D, bool BF16, bool X>
 struct DkdvL {
   static hipError_t run(const BwdProblem& p, hipStream_t s) {
-    if constexpr (D == 256) {
-      return p.bias ? hipErrorInvalidValue : launch_dkdv_t<D, BF16, X, false>(p, s);
-    } else {
-      return p.bias ? launch_dkdv_t<D, BF16, X, true>(p, s) : launch_dkdv_t<D, BF16, X, false>(p, s);
-    }
+    return p.bias ? launch_dkdv_t<D, BF16, X, true>(p, s) : launch_dkdv_t<D, BF16, X, false>(p, s);
   }
 };
 template <int D, bool BF16, bool X>
 struct DqL {
   static hipError_t run(const BwdProblem& p, hipStream_t s) {
-    if constexpr (D == 256) {
-      return p.bias ? hipErrorInvalidValue : launch_dq_t<D, BF16, X, false>(p, s);
-    } else {
-      return p.bias ? launch_dq_t<D, BF16, X, true>(p, s) : launch_dq_t<D, BF16, X, false>(p, s);
-    }
+    return p.bias ? launch_dq_t<D, BF16, X, true>(p, s) : launch_dq_t<D, BF16, X, false>(p, s);
   }
 };
 

@@ -14,8 +14,7 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Head dimensions: 64, 128 and 256 everywhere except the backward with an
-// attention bias (64 and 128: at d=256 its LDS stages would not fit).
+// Head dimensions: 64, 128 and 256 everywhere.
 bool head_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
 // The kernels address one head's rows through a buffer resource with a 32-bit
@@ -305,7 +304,6 @@ int flash_attn_bwd_bias(const void* q, const void* k, const void* v, const void*
   if (!q || !k || !v || !bias || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_common(B, H, N, d, scale, causal, dtype, false);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_HEADDIM;
   if (N > 46340 || bias_stride_b < 0 || bias_stride_h < 0) return FA_ERR_SHAPE;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
@@ -494,7 +492,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_SHAPE:
       return "invalid shape (B, H, N must be >= 1, tensors < 2^31 elements, (N+256)*d*(output element "
              "bytes) < 2^32 per head, causal 0/1)";
-    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (64 or 128 for the backward with a bias)";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_DTYPE: return "unknown dtype code";
     case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -202,7 +202,7 @@ def test_fwd_bias_validation(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bias=None), 1), (dict(dv=None), 1), (dict(N=0), 2), (dict(N=46344), 2),
-    (dict(bias_stride_h=-8), 2), (dict(d=48), 3), (dict(d=256), 3), (dict(dtype=9), 4), (dict(bias=P + 8), 5),
+    (dict(bias_stride_h=-8), 2), (dict(d=48), 3), (dict(dtype=9), 4), (dict(bias=P + 8), 5),
     (dict(N=20), 5), (dict(bias_stride_b=12), 5), (dict(workspace=None), 7),
     (dict(workspace_bytes=8 * 8 - 1), 7), (dict(scale=float("inf")), 8),
 ])

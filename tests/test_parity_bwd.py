@@ -231,7 +231,7 @@ def check_bias_grads(w, bias_bits, res, tag=""):
 
 @pytest.mark.parametrize("fmt,out_f32", [(si.FMT_F16, False), (si.FMT_BF16, True)])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N", [8, 64, 136, 264])
 @pytest.mark.parametrize("layout", ["shared", "per_batch_head"])
 def test_bias_bwd_random(N, d, causal, fmt, out_f32, layout):
