@@ -210,17 +210,24 @@ constexpr int kDkvBQ = 64;     // query rows per streamed tile (d <= 128)
 // d=256 streams 32-row tiles: its K/V fragments take 128 registers per lane
 // and its dK/dV accumulators 256 (in the accumulation registers), which
 // leaves room for one 32-row tile's scores and dP only.
-template <int D>
-__host__ __device__ constexpr int dkdv_bq() { return D == 256 ? 32 : kDkvBQ; }
+// d=128 (unbiased, except fp16 causal) streams 32-row tiles as well: the
+// smaller score and dP tiles let the non-causal kernels run two waves per
+// SIMD with nothing parked in the accumulation registers (B2 H12 N4096:
+// -11% fp16, -14% bf16; bf16 causal -4%; fp16 causal measured +3% and keeps
+// 64 rows, as do the bias kernels).
+template <int D, bool BF16, bool CAUSAL, bool BIAS>
+__host__ __device__ constexpr int dkdv_bq() {
+  return D == 256 ? 32 : (D == 128 && !BIAS && !(CAUSAL && !BF16)) ? 32 : kDkvBQ;
+}
 
-template <int D>
+template <int D, int BQ>
 __host__ __device__ constexpr int dkdv_stage_bytes() {
-  return 2 * dkdv_bq<D>() * D * 2 + 2 * dkdv_bq<D>() * 4;  // Q, dO tiles + LSE2, D rows
+  return 2 * BQ * D * 2 + 2 * BQ * 4;  // Q, dO tiles + LSE2, D rows
 }
 
 template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BQ = dkdv_bq<D>();
+  constexpr int BQ = dkdv_bq<D, BF16, CAUSAL, BIAS>();
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int QT = BQ / 32;  // 32-row query sub-tiles per streamed tile
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
   // before each LDS read).
   constexpr bool kCounted = BIAS || FA_BWD_COUNTED || (D == 128 && !CAUSAL) || (D == 256 && FA_BWD256_COUNTED);
   constexpr bool kBiasLds = BIAS;
-  constexpr int STAGE = dkdv_stage_bytes<D>();
+  constexpr int STAGE = dkdv_stage_bytes<D, BQ>();
   constexpr int TILE = BQ * ROWB;
   // fp16: K is pre-multiplied by c = scale*log2(e) and the S accumulators
   // start at -LSE*log2(e) (as dP's start at -D), so the MFMAs produce the
@@ -632,23 +639,25 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
 constexpr int kDqRows = 128;
 // keys per streamed K/V tile (d=256: 32, for the same register reason as the
 // dK/dV kernel's 32-row tiles)
-template <int D>
-__host__ __device__ constexpr int dq_bk() { return D == 256 ? 32 : 64; }
+// (unbiased d=128 streams 32-key tiles too: -2% to -7%, the causal kernels
+// then running two waves per SIMD; bf16 non-causal +1.4%)
+template <int D, bool BIAS>
+__host__ __device__ constexpr int dq_bk() { return D == 256 ? 32 : (D == 128 && !BIAS) ? 32 : 64; }
 
-template <int D>
+template <int D, bool BIAS>
 __host__ __device__ constexpr int dq_stage_bytes() {
-  return 2 * dq_bk<D>() * D * 2;  // K, V tiles
+  return 2 * dq_bk<D, BIAS>() * D * 2;  // K, V tiles
 }
 // With a bias each wave stages its 32 rows of two key tiles' bias in LDS
 // (see bwd_dq_kernel), behind the two K/V stages.
 template <int D, bool BIAS>
 __host__ __device__ constexpr int dq_ring_bytes() {
-  return BIAS ? (kBwdThreads / 64) * 2 * 32 * dq_bk<D>() * 2 : 0;
+  return BIAS ? (kBwdThreads / 64) * 2 * 32 * dq_bk<D, BIAS>() * 2 : 0;
 }
 
 template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int BK = dq_bk<D>();
+  constexpr int BK = dq_bk<D, BIAS>();
   constexpr int DC = D / 16;
   constexpr int DT = D / 32;
   constexpr int KT = BK / 32;
@@ -657,7 +666,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dq_kernel
   constexpr int ROWB = D * 2;
   constexpr int LOADS = BK * CPR / kBwdThreads;
   static_assert(LOADS * kBwdThreads == BK * CPR, "tile split");
-  constexpr int STAGE = dq_stage_bytes<D>();
+  constexpr int STAGE = dq_stage_bytes<D, BIAS>();
   constexpr int TILE = BK * ROWB;
   // fp16: Q is pre-multiplied by c and the S accumulators start at
   // -LSE*log2(e) (this lane's row), as in the dK/dV kernel.
@@ -1024,7 +1033,8 @@ hipError_t launch_dkdv_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDkvKeys - 1) / kDkvKeys;
   // two stages, then (bias) each wave's two-slot ring of BQ rows x 64 bytes
-  const int lds = 2 * dkdv_stage_bytes<D>() + (BIAS ? (kBwdThreads / 64) * 2 * dkdv_bq<D>() * 64 : 0);
+  constexpr int BQ = dkdv_bq<D, BF16, CAUSAL, BIAS>();
+  const int lds = 2 * dkdv_stage_bytes<D, BQ>() + (BIAS ? (kBwdThreads / 64) * 2 * BQ * 64 : 0);
   auto kern = bwd_dkdv_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
@@ -1036,7 +1046,7 @@ template <int D, bool BF16, bool CAUSAL, bool BIAS>
 hipError_t launch_dq_t(const BwdProblem& p, hipStream_t stream) {
   BwdArgs a = make_args(p);
   a.n_tiles = (p.N + kDqRows - 1) / kDqRows;
-  const int lds = 2 * dq_stage_bytes<D>() + dq_ring_bytes<D, BIAS>();
+  const int lds = 2 * dq_stage_bytes<D, BIAS>() + dq_ring_bytes<D, BIAS>();
   auto kern = bwd_dq_kernel<D, BF16, CAUSAL, BIAS>;
   hipError_t e = set_lds(kern, lds);
   if (e != hipSuccess) return e;
