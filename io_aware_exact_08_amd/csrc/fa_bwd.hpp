@@ -214,10 +214,15 @@ constexpr int kDkvBQ = 64;     // query rows per streamed tile (d <= 128)
 // smaller score and dP tiles let the non-causal kernels run two waves per
 // SIMD with nothing parked in the accumulation registers (B2 H12 N4096:
 // -11% fp16, -14% bf16; bf16 causal -4%; fp16 causal measured +3% and keeps
-// 64 rows, as do the bias kernels).
+// 64 rows, as do the bias kernels).  So does the unbiased non-causal d=64
+// one, which then runs three waves per SIMD (165 VGPRs): -6% at B2 H12
+// N4096, -1% at N8192; its causal kernels measured 6-16% slower.
 template <int D, bool BF16, bool CAUSAL, bool BIAS>
 __host__ __device__ constexpr int dkdv_bq() {
-  return D == 256 ? 32 : (D == 128 && !BIAS && !(CAUSAL && !BF16)) ? 32 : kDkvBQ;
+  return D == 256 ? 32
+       : (D == 128 && !BIAS && !(CAUSAL && !BF16)) ? 32
+       : (D == 64 && !BIAS && !CAUSAL)              ? 32
+                                                    : kDkvBQ;
 }
 
 template <int D, int BQ>
