@@ -136,8 +136,8 @@ def traffic_summary(fetch_csv, write_csv, out_path, calib_mib):
 
 def config_sweep(fa, si, torch, np, dev):
     """Event-timed forward (and backward where the configuration has one) of the
-    other synthetic configurations; reported beside the headline step, outside
-    its timed region."""
+    other synthetic configurations, as graph replays (see `timed`); reported
+    beside the headline step, outside its timed region."""
     out = {}
 
     def tensors(w):
@@ -145,7 +145,9 @@ def config_sweep(fa, si, torch, np, dev):
         conv = lambda b: torch.from_numpy(b.view(np.int16)).view(dt).to(dev)  # noqa: E731
         return conv(w.q), conv(w.k), conv(w.v), (conv(w.do) if w.do is not None else None)
 
-    def timed(fn, reps):
+    how = {}
+
+    def timed(fn, reps, outs=()):
         # the clocks need about 0.2 s of sustained load to settle
         t0 = time.perf_counter()
         n = 0
@@ -156,11 +158,42 @@ def config_sweep(fa, si, torch, np, dev):
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # The calls go through the Python binding, whose host time per call
+        # (several microseconds) would show in the small shapes' kernel time:
+        # time replays of a captured graph of `reps` calls instead (the same
+        # launches, no host work between them).  Eager calls if capture fails
+        # or a replay's outputs differ from the eager call's.
+        ref = [t.clone() for t in outs]
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            replays = 3
+            e0.record()
+            for _ in range(replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if all(torch.equal(t, r) for t, r in zip(outs, ref)):
+                how["timing"] = "graph"
+                return e0.elapsed_time(e1) / (reps * replays)
+        except Exception:
+            torch.cuda.synchronize()
         e0.record()
         for _ in range(reps):
             fn()
         e1.record()
         torch.cuda.synchronize()
+        how["timing"] = "eager"
         return e0.elapsed_time(e1) / reps
 
     def run(name, w, out_f32=False, bwd=False, reps=20, splits=None, bias_bits=None):
@@ -172,8 +205,9 @@ def config_sweep(fa, si, torch, np, dev):
             dt = torch.float16 if w.fmt == "f16" else torch.bfloat16
             bias = torch.from_numpy(bias_bits.view(np.int16)).view(dt).to(dev)
             ms = timed(lambda: fa.flash_attn_fwd_bias(q, k, v, bias, causal=w.causal, scale=w.scale,
-                                                      out_f32=out_f32, o=o, lse=lse), reps)
+                                                      out_f32=out_f32, o=o, lse=lse), reps, (o, lse))
             rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal, "bias": list(bias.shape),
+                   "timing": how.get("timing"),
                    "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                    "fwd_frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
             if bwd:
@@ -182,7 +216,7 @@ def config_sweep(fa, si, torch, np, dev):
                 dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
                 ms_b = timed(lambda: fa.flash_attn_bwd_bias(q, k, v, bias, o, lse, do,
                                                             causal=w.causal, scale=w.scale, dq=dq,
-                                                            dk=dk, dv=dv, workspace=ws), reps)
+                                                            dk=dk, dv=dv, workspace=ws), reps, (dq, dk, dv))
                 rec["bwd_ms"] = round(ms_b, 4)
                 rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
                 # executed work: dK/dV 8 and dQ 6 BHN^2d products = 3.5x the forward's
@@ -191,15 +225,15 @@ def config_sweep(fa, si, torch, np, dev):
             return
         if splits is None:
             ms = timed(lambda: fa.flash_attn_fwd(q, k, v, causal=w.causal, scale=w.scale,
-                                                 out_f32=out_f32, o=o, lse=lse), reps)
+                                                 out_f32=out_f32, o=o, lse=lse), reps, (o, lse))
         else:
             # splits == 0: the library's automatic plan
             ws = torch.empty(max(fa._lib.flash_attn_fwd_splitkv_workspace_bytes(B, H, N, d, splits) // 4, 1),
                              dtype=torch.float32, device=dev)
             ms = timed(lambda: fa.flash_attn_fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale,
                                                          out_f32=out_f32, num_splits=splits,
-                                                         o=o, lse=lse, workspace=ws), reps)
-        rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal,
+                                                         o=o, lse=lse, workspace=ws), reps, (o, lse))
+        rec = {"shape": [B, H, N, d], "dtype": w.fmt, "causal": w.causal, "timing": how.get("timing"),
                "fwd_ms": round(ms, 4), "fwd_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                "fwd_frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)}
         if splits is not None:
@@ -210,7 +244,7 @@ def config_sweep(fa, si, torch, np, dev):
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
             ms_b = timed(lambda: fa.flash_attn_bwd(q, k, v, o, lse, do, causal=w.causal,
                                                    scale=w.scale, dq=dq, dk=dk, dv=dv,
-                                                   workspace=ws), reps)
+                                                   workspace=ws), reps, (dq, dk, dv))
             rec["bwd_ms"] = round(ms_b, 4)
             rec["bwd_tflops_credited"] = round(2.5 * fl / (ms_b * 1e-3) / 1e12, 1)
             rec["bwd_frac_of_peak"] = round(3.5 * fl / (ms_b * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4)
