@@ -89,7 +89,12 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
   double best_cost = rounds(items);
   const double unsplit = best_cost;
   const int smax = std::min(16, key_tiles / 4);  // each split keeps at least 4 key tiles
-  for (int S = 2; S <= smax; ++S) {
+  // Below 64 key tiles per row the float32 partials and the merge launch cost
+  // more than the model's 8 tiles: a uniform split then loses. Above half the
+  // slots the only gain the model sees is a partial last round, which it
+  // overprices (below), so only grids of at most half the slots split evenly.
+  const int smax_uniform = key_tiles >= 64 && items * 2 <= slots ? smax : 1;
+  for (int S = 2; S <= smax_uniform; ++S) {
     const double c = rounds(items * S) * (1.0 / S + overhead) + merge_fixed + merge_rows;
     if (c < best_cost && c < 0.97 * unsplit) {
       best_cost = c;
@@ -98,7 +103,10 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
     }
   }
   const long long full = (items / slots) * slots, r = items - full;
-  if (full > 0 && r > 0) {
+  // A last round of up to one workgroup per compute unit runs each of them
+  // without a co-resident workgroup, faster than the model's full round, so
+  // the tail is split only while it fills at most a quarter of the slots.
+  if (full > 0 && r > 0 && r * 4 <= slots) {
     for (int S = 2; S <= smax; ++S) {
       const double c = (double)(full / slots) + rounds(r * S) * (1.0 / S + overhead) + merge_fixed +
                        merge_rows * (double)r / (double)items;

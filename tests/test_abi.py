@@ -277,8 +277,11 @@ def test_splitkv_automatic_plan_workspace(lib):
     # whole rounds (1536 items = 3 x 512) and short key ranges: no split
     assert ws(2, 12, 8192, 64, 0) == 0
     assert ws(2, 12, 1024, 64, 0) == 0
-    # 768 items = 1.5 rounds: the last 256 items (rows from head 16 on) split in two
-    assert ws(2, 12, 4096, 64, 0) == 2 * (24 * 4096 - 16 * 4096) * 65 * 4
+    # 768 items = 1.5 rounds: a last round of one workgroup per compute unit
+    # stays unsplit
+    assert ws(2, 12, 4096, 64, 0) == 0
+    # 32 key tiles of 32 keys at d=128: too short to split
+    assert ws(2, 12, 1024, 128, 0) == 0
     # 1560 items: 1536 unsplit, the last 24 (from head 23, tile 41) in 16
     rows = 24 * 8200 - (23 * 8200 + 41 * 128)
     assert ws(2, 12, 8200, 64, 0) == 16 * rows * 65 * 4
@@ -287,7 +290,7 @@ def test_splitkv_automatic_plan_workspace(lib):
 
 
 def test_splitkv_automatic_plan_rejects_bad_workspace(lib):
-    args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=64, B=2, H=12, N=4096,
+    args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=64, B=2, H=12, N=8200,
                 d=64, scale=0.125, causal=0, dtype=0, num_splits=0, stream=None)
     assert lib.flash_attn_fwd_splitkv(**args) == 7
     args.update(workspace=None, workspace_bytes=0)

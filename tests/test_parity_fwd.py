@@ -341,7 +341,7 @@ def test_bias_hidden_first_tiles_low_logits_f16(kind):
 
 
 @pytest.mark.parametrize("B,H,N,d,fmt,causal,out_f32", [
-    (2, 12, 4096, 64, si.FMT_F16, False, False),   # 1.5 rounds: the last 256 tiles split in two
+    (2, 12, 4096, 64, si.FMT_F16, False, False),   # 1.5 rounds: half a round, no split
     (2, 12, 8200, 64, si.FMT_F16, False, False),   # ragged N: 1536 tiles whole, the last 24 in 16
     (1, 4, 8192, 128, si.FMT_BF16, False, True),   # half a round: every tile split in two
     (2, 12, 1024, 64, si.FMT_F16, False, False),   # short key range: no split
