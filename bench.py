@@ -28,7 +28,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic_B2H12N8192d64_f16.
 KERNEL_SOURCES = sorted(os.path.join("io_aware_exact_08_amd", "csrc", f)
                         for f in os.listdir(os.path.join(ROOT, "io_aware_exact_08_amd", "csrc"))
                         if f.endswith((".hip", ".hpp")))
-# host worker processes for the CPU oracle: the GPU machine's CPU share per GPU
+# host worker processes for the CPU oracle: at most the host cores a single-GPU node gives each GPU
 MAX_CPU_WORKERS = 16
 
 
