@@ -145,6 +145,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_byte_addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// The same read at a 32-bit LDS byte address.  A caller that keeps a
+// per-lane base in a register and adds a constant below 2^16 gets the
+// constant folded into the instruction's offset field.
+__device__ __forceinline__ u32x2 lds_read_tr16_at(uint32_t lds_byte_addr) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)lds_byte_addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Two floats -> two 16-bit values in one dword, round-to-nearest-even.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {

@@ -132,14 +132,23 @@ __global__ __launch_bounds__(kTQ16, q16_min_waves<D>()) void fwd_q16_kernel(FwdA
   // d = 16dt + 4q .. +3, i.e. chunk 2dt + q/2 at position
   // (2dt + q/2) ^ 2(key & 7), bytes (q & 1) * 8; lane i then receives
   // d = 16dt + i for those four keys.
-  int vr[8];
+  // The V array starts 64 KB into LDS at d = 256, past what a read's 16-bit
+  // offset field reaches, so each lane keeps its eight offsets with the
+  // array's address already added (hidden from the compiler, which would
+  // otherwise add the array's address back on every read); a read then adds
+  // only the stage and window constants, which its offset field holds.
+  uint32_t va[8];
   {
+    const uint32_t lds_v0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0];
     const int j = m >> 2, q = m & 3, key = 4 * g + j;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      vr[i] = key * ROWB + (((2 * i + (q >> 1)) ^ ((key & 7) << 1)) * 16) + (q & 1) * 8;
+    for (int i = 0; i < 8; ++i) {
+      va[i] = lds_v0 + (uint32_t)(key * ROWB + (((2 * i + (q >> 1)) ^ ((key & 7) << 1)) * 16) + (q & 1) * 8);
+      asm volatile("" : "+v"(va[i]));
+    }
   }
-  auto v_off = [&](int dt) { return vr[dt & 7] + (dt >> 3) * 256; };
+  static_assert((kStQ16 - 1) * BK * ROWB + (D / 16 - 1) / 8 * 256 + 16 * ROWB + 8 < 65536,
+                "V read constants fit the offset field");
 
   // Direct-load slots: thread slot p = i * kTQ16 + tid holds tile row p / CPR
   // at chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
@@ -207,11 +216,12 @@ __global__ __launch_bounds__(kTQ16, q16_min_waves<D>()) void fwd_q16_kernel(FwdA
   };
   // O^T += V^T P^T for the packed probabilities pf (k-slot i: key
   // 4g + i for i < 4, 16 + 4g + i - 4 after).
-  auto pv = [&](const char* Vb, const u32x4& pf) {
+  auto pv = [&](uint32_t vst, const u32x4& pf) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const u32x2 lo = lds_read_tr16(Vb + v_off(dt));
-      const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + 16 * ROWB);
+      const uint32_t at = va[dt & 7] + vst + (uint32_t)((dt >> 3) * 256);
+      const u32x2 lo = lds_read_tr16_at(at);
+      const u32x2 hi = lds_read_tr16_at(at + 16 * ROWB);
       const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
       oacc[dt] = mfma16<BF16>(vf, pf, oacc[dt]);
       pin_step<2, 2, LA>(dt);
@@ -270,12 +280,12 @@ __global__ __launch_bounds__(kTQ16, q16_min_waves<D>()) void fwd_q16_kernel(FwdA
     l_run = __builtin_fmaf(l_run, alpha, ts);
     if constexpr (BF16) l32_run = __builtin_fmaf(l32_run, alpha, ts32);
   };
-  auto rescale_pv = [&](const char* Vb, const u32x4& pf, float alpha, bool grow) {
+  auto rescale_pv = [&](uint32_t vst, const u32x4& pf, float alpha, bool grow) {
     if (__ballot(grow) != 0ull) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
-    pv(Vb, pf);
+    pv(vst, pf);
   };
 
   // Pipeline: iteration j (tile j in stage j % 4) starts tile j + 3's loads,
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(kTQ16, q16_min_waves<D>()) void fwd_q16_kernel(FwdA
         s_next = scores((const char*)sK[st1]);
         softmax(std::false_type{}, s_cur, k0, pf, alpha, grow);
       }
-      rescale_pv((const char*)sV[st], pf, alpha, grow);
+      rescale_pv((uint32_t)(st * STAGEB), pf, alpha, grow);
       s_cur = s_next;
     }
     if (j + kAhead < n_kt) {
