@@ -355,6 +355,33 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
     }
   }
   auto v_off = [&](int dt) { return v_tr[dt % RDT] + (dt / RDT) * 256; };
+  // With the bias ring at d = 64 the compiler places the V array 64 KB or
+  // more into LDS, beyond a read's 16-bit offset field, and then adds the
+  // array's address with a VALU op before every read.  Those kernels keep the
+  // address in the per-lane bases (hidden from the compiler) instead.
+  constexpr bool kVBase = kBiasLds && D == 64;
+  uint32_t v_ta[kVBase ? RDT : 1];
+  if constexpr (kVBase) {
+#pragma unroll
+    for (int dt = 0; dt < RDT; ++dt) {
+      v_ta[dt] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)&sV[0][0] + (uint32_t)v_tr[dt];
+      asm volatile("" : "+v"(v_ta[dt]));
+    }
+    static_assert((kStages - 1) * BK * ROWB + (DT / RDT - 1) * 256 + (KC - 1) * 16 * ROWB + 4 * ROWB + 8 < 65536,
+                  "V read constants fit the offset field");
+  }
+  // V^T operand of d tile dt and 16-key chunk kc from the stage at Vb
+  auto v_read = [&](const char* Vb, int dt, int kc, u32x2& lo, u32x2& hi) {
+    if constexpr (kVBase) {
+      const uint32_t at = v_ta[dt % RDT] + (uint32_t)(Vb - (const char*)&sV[0][0]) +
+                          (uint32_t)((dt / RDT) * 256 + kc * 16 * ROWB);
+      lo = lds_read_tr16_at(at);
+      hi = lds_read_tr16_at(at + 4 * ROWB);
+    } else {
+      lo = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB);
+      hi = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB + 4 * ROWB);
+    }
+  };
   // Direct-load slots: thread slot p = i*256 + tid holds tile row p / CPR at
   // swizzled chunk position p % CPR, i.e. global chunk (p % CPR) ^ swz(row).
   uint32_t k_gl[LOADS], v_gl[LOADS];
@@ -529,8 +556,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x2 lo = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB);
-          const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB + 4 * ROWB);
+          u32x2 lo, hi;
+          v_read(Vb, dt, kc, lo, hi);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
@@ -753,8 +780,8 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const u32x2 lo = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB);
-          const u32x2 hi = lds_read_tr16(Vb + v_off(dt) + kc * 16 * ROWB + 4 * ROWB);
+          u32x2 lo, hi;
+          v_read(Vb, dt, kc, lo, hi);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][dt] = mfma32<BF16>(vf, pf[qb][kc], oacc[qb][dt]);
