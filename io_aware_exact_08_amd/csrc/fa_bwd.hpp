@@ -13,10 +13,10 @@
 // Three kernels, all deterministic (no atomics):
 //  * bwd_pre   : -D and -LSE*log2(e) for every row (one pass over O and dO).
 //  * bwd_dkdv  : a workgroup keeps 128 keys of K and V in registers (32 per
-//                wave) and loops over 64-row Q/dO tiles (the loop order
-//                above); dK and dV accumulate in registers.
+//                wave) and loops over Q/dO tiles of 32 or 64 rows (dkdv_bq;
+//                the loop order above); dK and dV accumulate in registers.
 //  * bwd_dq    : a workgroup keeps 128 query rows of Q and dO in registers and
-//                loops over 64-key K/V tiles.
+//                loops over K/V tiles of 32 or 64 keys (dq_bk).
 // Mapping onto CDNA4, as in the forward: v_mfma_f32_32x32x16 with the
 // accumulator of one product feeding the next as its B operand after
 // rounding; streamed tiles arrive by direct buffer->LDS loads into two
@@ -203,10 +203,10 @@ constexpr int bwd_min_waves() { return D == 64 ? 2 : 1; }
 #endif
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup owns 128 keys (32 per wave); loop over 64-row query tiles.
+// dK, dV: workgroup owns 128 keys (32 per wave); loop over query tiles.
 // ---------------------------------------------------------------------------
 constexpr int kDkvKeys = 128;  // keys per workgroup
-constexpr int kDkvBQ = 64;     // query rows per streamed tile (d <= 128)
+constexpr int kDkvBQ = 64;     // query rows per streamed tile, unless 32 below
 // d=256 streams 32-row tiles: its K/V fragments take 128 registers per lane
 // and its dK/dV accumulators 256 (in the accumulation registers), which
 // leaves room for one 32-row tile's scores and dP only.
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(kBwdThreads, bwd_min_waves<D>()) void bwd_dkdv_kern
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup owns 128 query rows (32 per wave); loop over 64-key tiles.
+// dQ: workgroup owns 128 query rows (32 per wave); loop over key tiles.
 // ---------------------------------------------------------------------------
 constexpr int kDqRows = 128;
 // keys per streamed K/V tile (d=256: 32, for the same register reason as the
