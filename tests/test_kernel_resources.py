@@ -13,7 +13,7 @@ from io_aware_exact_08_amd import build
 HOT = [
     "void fa::fwd_kernel<64, false, false, false, false, false>(fa::FwdArgs)",   # fp16 A100 shape
     "void fa::fwd_kernel<64, false, true, false, false, false>(fa::FwdArgs)",    # fp16 causal
-    "void fa::fwd_q16_kernel<128, true, true, true, false>(fa::FwdArgs)",        # spiked bf16 causal
+    "void fa::fwd_kernel<128, true, true, true, false, false>(fa::FwdArgs)",     # spiked bf16 causal
     "void fa::fwd_kernel<64, true, true, false, false, false>(fa::FwdArgs)",     # long bf16 causal
     "void fa::bwd_dkdv_kernel<64, false, false, false>(fa::BwdArgs)",
     "void fa::bwd_dkdv_kernel<64, false, true, false>(fa::BwdArgs)",
@@ -70,8 +70,8 @@ Q16 = [(256, f"void fa::fwd_q16_kernel<256, {bf}, {c}, {o}, false>(fa::FwdArgs)"
        for bf in ("false", "true") for c in ("false", "true") for o in ("false", "true")]
 Q16 += [(256, f"void fa::fwd_q16_kernel<256, {bf}, {c}, false, true>(fa::FwdArgs)")
         for bf in ("false", "true") for c in ("false", "true")]
-Q16 += [(128, f"void fa::fwd_q16_kernel<128, true, {c}, {o}, false>(fa::FwdArgs)")
-        for c in ("false", "true") for o in ("false", "true")]
+Q16 += [(128, f"void fa::fwd_q16_kernel<128, true, false, {o}, false>(fa::FwdArgs)")
+        for o in ("false", "true")]
 Q16 += [(128, f"void fa::fwd_q16_kernel<128, true, {c}, false, true>(fa::FwdArgs)")
         for c in ("false", "true")]
 
