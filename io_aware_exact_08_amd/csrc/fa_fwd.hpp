@@ -90,7 +90,8 @@ namespace fa {
 // -12% (bf16 causal, fp32 O), bit-identical.
 // Unbiased d=256 forwards (plain and split-KV) run fwd_q16_kernel
 // (fa_fwd_q16.hpp); fwd_kernel<256> serves the biased one.  FA_FWD128_Q16
-// routes the unbiased d=128 forwards there too.
+// routes the unbiased non-causal bf16 d=128 forwards and every bf16 d=128
+// split there too.
 #ifndef FA_FWD128_Q16
 #define FA_FWD128_Q16 1
 #endif

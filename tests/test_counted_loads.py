@@ -1,5 +1,5 @@
 """The bias kernels (d = 64, 128) and the 16-query-wave forward (d = 256 and
-bf16 d = 128) issue the direct loads of their key or query loop as inline
+non-causal bf16 d = 128) issue the direct loads of their key or query loop as inline
 assembly and count the waits themselves.  The compiler does not see those
 loads, so any vmcnt wait it inserted inside the loop would miscount them (and
 a vmcnt(0) would drain the whole pipeline).  Compile the d = 64 forward and

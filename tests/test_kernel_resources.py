@@ -62,8 +62,8 @@ def test_bias_forwards_do_not_spill(report, name):
     assert r["scratch_bytes_per_lane"] == 0, (name, r)
 
 
-# The 16-query-wave forward (every unbiased d = 256 one, the bf16 d = 128
-# ones; plain and split-KV) counts its K/V loads the same way.  Its workgroup
+# The 16-query-wave forward (every unbiased d = 256 one; the non-causal bf16
+# d = 128 ones and every bf16 d = 128 split) counts its K/V loads the same way.  Its workgroup
 # is eight waves, so it needs two waves per SIMD at d = 256 (one workgroup per
 # CU) and four at d = 128 (two).
 Q16 = [(256, f"void fa::fwd_q16_kernel<256, {bf}, {c}, {o}, false>(fa::FwdArgs)")
