@@ -79,8 +79,10 @@ namespace fa {
 // Hand-counted direct loads for the unbiased d <= 128 forwards too (the
 // compiler's own waits drained the next tile's loads before the first K read
 // of every iteration).  Same-box A/B, bit-identical: B2 H12 N8192 d64 fp16
-// -1.3 to -3.8%, bf16 -0.8%, d128 B2 H12 N4096 fp16 -7.7% and bf16 -4%; the
-// fp16 causal d=64 kernel measured +0.9 to +1.5% and keeps the compiler's.
+// -1.3 to -3.8%, bf16 -0.8%, d128 B2 H12 N4096 fp16 -7.7% and bf16 -4%.  The
+// fp16 causal d=64 kernel measured +0.9 to +1.5% with them alone, and -2.5%
+// (B1 H8 N16384), -9% (B2 H12 N2048, fp32 O) and +0.7% (B2 H12 N4096) with
+// them and the mask-free loop below the diagonal together.
 #ifndef FA_FWD_COUNTED
 #define FA_FWD_COUNTED 1
 #endif
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // gives up one stage for the ring, so two workgroups still fit a CU.
   constexpr bool kCounted =
       BIAS ? D <= 128
-           : (FA_FWD_COUNTED && !SPLITKV && !(D == 64 && CAUSAL && !BF16) && (D <= 128 || FA_FWD256_COUNTED));
+           : (FA_FWD_COUNTED && !SPLITKV && (D <= 128 || FA_FWD256_COUNTED));
   constexpr bool kBiasLds = BIAS && kCounted;
   constexpr int kStages = (kBiasLds && D == 64) ? 3 : FwdCfg<D>::STAGES;
   static_assert(kStages == 3 || kStages == 4, "the pipeline below runs three or four stages");
@@ -935,10 +937,12 @@ __global__ __launch_bounds__(kThreads, FwdCfg<D>::MIN_WAVES) void fwd_kernel(Fwd
   // workgroup (global tile t with (t + 1) BK - 1 <= qt BQ) and inside N run a
   // loop body without masks or active checks.  Measured (same box, outputs
   // bit-identical): bf16 d=64 causal -2.6% (B1 H8 N32768) and -3.7% (B2 H12
-  // N4096), fp16 d=128 causal -1.8%; fp16 d=64 causal +1.9%, so that one
-  // keeps the single loop, as do the bias kernels (not measured) and the
-  // split-KV ones (where the second body cost a spilled register).
-  constexpr bool kCleanLoop = CAUSAL && !BIAS && !SPLITKV && D <= 128 && !(D == 64 && !BF16);
+  // N4096), fp16 d=128 causal -1.8%; fp16 d=64 causal +1.9% with the
+  // compiler's load waits and -2.5 to -9% (+0.7% at B2 H12 N4096) with the
+  // hand-counted ones, which it now takes.  The bias kernels (not measured)
+  // and the split-KV ones (where the second body cost a spilled register)
+  // keep the single loop.
+  constexpr bool kCleanLoop = CAUSAL && !BIAS && !SPLITKV && D <= 128;
   if constexpr (kCleanLoop) {
     const int n_clean = min(n_kt, max(0, min((qt * BQ + 1) / BK, N / BK) - j0));
     for (; j + kStages <= n_clean; j += kStages) {
