@@ -62,6 +62,20 @@ def test_small_shapes(N, d, causal, fmt, out_f32):
     check(w, o, lse)
 
 
+@pytest.mark.parametrize("fmt,d", [(si.FMT_F16, 64), (si.FMT_BF16, 64), (si.FMT_F16, 128), (si.FMT_BF16, 128)])
+@pytest.mark.parametrize("N", [700, 1000, 1536])
+def test_causal_fully_visible_rounds(N, d, fmt):
+    """Causal forwards run whole rounds (four key tiles) of tiles that every
+    row of the 128-row workgroup sees through a loop body without masks, then
+    the rest (a partial round, the diagonal, a ragged end) through the masked
+    one.  Query tile qt has 2 qt such tiles at d = 64 (a partial round left
+    over when qt is odd) and 4 qt at d = 128; the last tiles of N = 700 and
+    1000 are ragged, N = 1536 is not.  Every element against the oracle."""
+    w = si.random_case(1, 2, N, d, fmt, True, seed=N + 3 * d + (fmt == si.FMT_BF16))
+    o, lse = run_fwd(w)
+    check(w, o, lse)
+
+
 @pytest.mark.parametrize("N", [1024, 2048, 4096, 8192])
 def test_a100_shape_full(N):
     """B=2 H=12 d=64 fp16 non-causal at the A100 table's shape, in the
