@@ -52,7 +52,8 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype,
 //  - no split: ceil(items / slots) rounds;
 //  - every item split S ways along the keys (split-KV): each split item is 1/S
 //    of the work plus a fixed overhead (partial O written in fp32, pipeline
-//    fill) of about four key tiles, plus the merge pass;
+//    fill) of about four key tiles, plus the merge pass (a launch, and a read
+//    of S partial rows per output row);
 //  - tail split (non-causal): the whole rounds run unsplit and write O
 //    directly, and only the last round's items are split S ways.
 // A split plan must be 3% cheaper than no split.  Causal launches keep the
@@ -89,13 +90,18 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
   double best_cost = rounds(items);
   const double unsplit = best_cost;
   const int smax = std::min(16, key_tiles / 4);  // each split keeps at least 4 key tiles
+  // The merge reads S partial rows per output row: its cost grows with S.
   // Below 64 key tiles per row the float32 partials and the merge launch cost
-  // more than the model's 8 tiles: a uniform split then loses. Above half the
-  // slots the only gain the model sees is a partial last round, which it
-  // overprices (below), so only grids of at most half the slots split evenly.
-  const int smax_uniform = key_tiles >= 64 && items * 2 <= slots ? smax : 1;
+  // more than the model says, and a uniform split lost at B2 H12 N1024 d128
+  // (192 workgroups on 512 slots); grids that fill at most an eighth of the
+  // slots still gain from it (B1 H1 N1024 d256: 35.6 -> 20.3 us at S = 4).
+  // Above half the slots the only gain the model sees is a partial last
+  // round, which it overprices (below), so only grids of at most half the
+  // slots split evenly.
+  const bool short_keys = key_tiles < 64;
+  const int smax_uniform = items * 2 <= slots && (!short_keys || items * 8 <= slots) ? smax : 1;
   for (int S = 2; S <= smax_uniform; ++S) {
-    const double c = rounds(items * S) * (1.0 / S + overhead) + merge_fixed + merge_rows;
+    const double c = rounds(items * S) * (1.0 / S + overhead) + merge_fixed + merge_rows * 0.5 * S;
     if (c < best_cost && c < 0.97 * unsplit) {
       best_cost = c;
       best.splits = S;
@@ -109,7 +115,7 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
   if (full > 0 && r > 0 && r * 4 <= slots) {
     for (int S = 2; S <= smax; ++S) {
       const double c = (double)(full / slots) + rounds(r * S) * (1.0 / S + overhead) + merge_fixed +
-                       merge_rows * (double)r / (double)items;
+                       merge_rows * 0.5 * S * (double)r / (double)items;
       if (c < best_cost && c < 0.97 * unsplit) {
         best_cost = c;
         best.splits = S;

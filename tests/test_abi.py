@@ -287,6 +287,11 @@ def test_splitkv_automatic_plan_workspace(lib):
     assert ws(2, 12, 8200, 64, 0) == 16 * rows * 65 * 4
     # 256 items on 512 slots: every item split in two
     assert ws(1, 4, 8192, 128, 0) == 2 * 4 * 8192 * 129 * 4
+    # a short key range on a nearly empty grid (8 items, 256 slots at d=256):
+    # four ways (the merge's cost grows with the split count)
+    assert ws(1, 1, 1024, 256, 0) == 4 * 1024 * 257 * 4
+    # 64 items of 16 key tiles on 512 slots: the overheads outweigh the gain
+    assert ws(1, 8, 1024, 64, 0) == 0
 
 
 def test_splitkv_automatic_plan_rejects_bad_workspace(lib):
