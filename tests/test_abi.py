@@ -290,8 +290,16 @@ def test_splitkv_automatic_plan_workspace(lib):
     # a short key range on a nearly empty grid (8 items, 256 slots at d=256):
     # four ways (the merge's cost grows with the split count)
     assert ws(1, 1, 1024, 256, 0) == 4 * 1024 * 257 * 4
-    # 64 items of 16 key tiles on 512 slots: the overheads outweigh the gain
-    assert ws(1, 8, 1024, 64, 0) == 0
+    # 64 items of 16 key tiles on 512 slots: the non-causal plan does not
+    # split (the overheads outweigh the gain); the causal one splits in two
+    # (8 key tiles per range of the heaviest item)
+    assert ws(1, 8, 1024, 64, 0) == 2 * 8 * 1024 * 65 * 4
+    # causal plans shorten the heaviest item on small grids: 4 ways for 8
+    # items of 32 key tiles, 8 ways for 64 items of 128 key tiles
+    plan = lib.flash_attn_fwd_splitkv_workspace_bytes
+    assert plan(1, 2, 4096, 128, 0) == 8 * 2 * 4096 * 129 * 4
+    # short key ranges on fuller grids stay unsplit
+    assert ws(2, 8, 1024, 128, 0) == 0
 
 
 def test_splitkv_automatic_plan_rejects_bad_workspace(lib):
