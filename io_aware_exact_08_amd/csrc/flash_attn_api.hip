@@ -86,13 +86,14 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
     // sets the launch's time when the grid is small.  Split every item into
     // the largest power of two S <= 8 that keeps items * S within one round
     // and at least 8 key tiles per range of the heaviest item; short key
-    // ranges (under 64 tiles) only on grids of at most an eighth of the
+    // ranges (under 2048 keys) only on grids of at most an eighth of the
     // slots, where the merge's fixed cost is repaid.  Measured (S=0 against
     // the fixed default): B1 H1 N1024 d256 37.2 -> 19.8 us, B1 H4 N1024 d128
-    // bf16 26.3 -> 18.3, B1 H4 N4096 d64 35.5 -> 29.6; splitting B2 H12 N1024
-    // d64 (192 items) or B2 H8 N1024 d128 (128 items) measured 10-30% slower.
+    // bf16 26.3 -> 18.3, B1 H4 N4096 d64 35.5 -> 29.6, B1 H8 N2048 d64 25.8
+    // -> 22.7; splitting B2 H12 N1024 d64 (192 items) or B2 H8 N1024 d128
+    // (128 items) measured 10-30% slower.
     int S = 1;
-    if (key_tiles >= 64 || items * 8 <= slots)
+    if (N >= 2048 || items * 8 <= slots)
       while (S < 8 && items * (2 * S) <= slots && key_tiles / (2 * S) >= 8) S *= 2;
     best.splits = std::max(S, flash_attn_fwd_splitkv_default_splits(1, BH, N, d, 1));
     return best;
