@@ -92,9 +92,16 @@ SplitPlan plan_splits(int BH, int N, int d, bool causal) {
     // bf16 26.3 -> 18.3, B1 H4 N4096 d64 35.5 -> 29.6, B1 H8 N2048 d64 25.8
     // -> 22.7; splitting B2 H12 N1024 d64 (192 items) or B2 H8 N1024 d128
     // (128 items) measured 10-30% slower.
+    // Past one workgroup per compute unit the split ranges share their units,
+    // which pays only over long key ranges: B2 H8 N2048 d64 (256 items)
+    // measured 26.2 us unsplit and 28.2 us in two, B1 H4 N4096 d64 (128
+    // items, 64 key tiles) 35.2 us in two and 29.6 us in four.
+    const long long cus = compute_units();
     int S = 1;
     if (N >= 2048 || items * 8 <= slots)
-      while (S < 8 && items * (2 * S) <= slots && key_tiles / (2 * S) >= 8) S *= 2;
+      while (S < 8 && items * (2 * S) <= slots && key_tiles / (2 * S) >= 8 &&
+             (items * (2 * S) <= cus || key_tiles >= 64))
+        S *= 2;
     best.splits = std::max(S, flash_attn_fwd_splitkv_default_splits(1, BH, N, d, 1));
     return best;
   }
