@@ -302,6 +302,29 @@ def test_splitkv_automatic_plan_workspace(lib):
     assert ws(2, 8, 1024, 128, 0) == 0
 
 
+def test_splitkv_causal_plan_choices(lib):
+    """The causal part of the automatic plan (assuming 256 compute units):
+    split counts read back from the workspace, which covers the larger of the
+    causal and non-causal plans.  The non-causal plan splits none of these
+    shapes except B1 H4 N4096 d64, where it too chooses four."""
+    ws = lib.flash_attn_fwd_splitkv_workspace_bytes
+
+    def splits(B, H, N, d):
+        return ws(B, H, N, d, 0) // (B * H * N * (d + 1) * 4)
+
+    # 128 items of 32 key tiles: two ranges keep one workgroup per CU; four
+    # would share the CUs over a short key range
+    assert splits(1, 8, 2048, 64) == 2
+    # 256 items already fill one workgroup per CU: no split
+    assert splits(2, 8, 2048, 64) == 0
+    # 128 items of 64 key tiles: sharing a CU pays over the long range
+    assert splits(1, 4, 4096, 64) == 4
+    # a grid of one round or more: only the fixed default (none here)
+    assert splits(2, 12, 4096, 64) == 0
+    # under 2048 keys on a grid over an eighth of the slots: no split
+    assert splits(2, 12, 1024, 64) == 0
+
+
 def test_splitkv_automatic_plan_rejects_bad_workspace(lib):
     args = dict(q=P, k=P, v=P, o=P, lse=P, workspace=P, workspace_bytes=64, B=2, H=12, N=8200,
                 d=64, scale=0.125, causal=0, dtype=0, num_splits=0, stream=None)
